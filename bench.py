@@ -1,0 +1,240 @@
+"""Benchmark of the Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+One step = one muon_step call over the whole workload (momentum + norm,
+normalise + cast, 5 x {Gram, Gram^2 epilogue, X update}, apply), with every
+input already resident in HBM.  Prints ONE JSON line:
+
+* value: nominal Newton-Schulz TFLOP/s of the whole step, counting
+  4 m^2 n + 2 m^3 per iteration and matrix (m the short side) over the step's
+  wall time;
+* matrices_per_s, NS-only TFLOP/s, fractions of the bf16 dense MFMA peak;
+* roofline: the dominant kernel's algorithmic work per launch over its
+  average launch time (HIP events on the launch stream, inside the timed
+  region) against its roofline;
+* cpu_baseline: the fp64 oracle timed on a bounded sample of the same
+  workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon step NS TFLOP/s + matrices/s at 1 GPU; % of bf16 MFMA peak"
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def phase_work(w):
+    """Algorithmic work of one launch of each phase over the workload:
+    flops for the MFMA phases (per Newton-Schulz iteration: X X^T 2 m^2 n,
+    A A 2 m^3, B X 2 m^2 n), HBM bytes for the elementwise ones (momentum:
+    read G and M, write M; normalise: read M, write bf16 X0; apply: read p
+    and bf16 O, write p)."""
+    gram = gram2 = xupd = 0
+    b_mom = b_norm = b_apply = 0
+    gsz = 2 if w.grad_dtype == "bf16" else 4
+    for r, c in w.shapes:
+        m, n = min(r, c), max(r, c)
+        gram += 2 * m * m * n
+        gram2 += 2 * m ** 3
+        xupd += 2 * m * m * n
+        e = r * c
+        b_mom += e * (gsz + 8)
+        b_norm += e * (4 + 2)
+        b_apply += e * (4 + 2 + 4)
+    return {"momentum_norm": ("hbm", b_mom), "normalize_cast": ("hbm", b_norm),
+            "gram": ("mfma", gram), "gram2_epilogue": ("mfma", gram2),
+            "x_update": ("mfma", xupd), "apply": ("hbm", b_apply)}
+
+
+def cpu_baseline(w, target_s: float = 20.0):
+    """The fp64 oracle on a bounded sample of the workload's matrices, timed
+    on this host's cores.  Returns the dict of the JSON line."""
+    from oracle import muon_oracle as O
+    from matrix_aware_optimizer_libmuon_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    # sample: distinct shapes in workload order, smallest first, until the
+    # estimated fp64 work would exceed the time target (>= 1 matrix)
+    seen, order = set(), []
+    for i, s in enumerate(w.shapes):
+        if s not in seen:
+            seen.add(s)
+            order.append(i)
+    order.sort(key=lambda i: w.shapes[i][0] * w.shapes[i][1])
+    t0 = time.perf_counter()
+    flops = 0
+    done = []
+    for idx in order:
+        mi = W.matrix_inputs(w, idx)
+        r, c = w.shapes[idx]
+        m, n = min(r, c), max(r, c)
+        ts = time.perf_counter()
+        O.muon_step_matrix(mi.param, mi.grad, mi.mom, lr=w.lr, mu=w.mu, wd=w.wd,
+                           ns_steps=w.ns_steps, eps=w.eps, rms_mode=w.rms_mode)
+        t0 += 0  # generation time is excluded below
+        done.append((idx, time.perf_counter() - ts))
+        flops += w.ns_steps * (4 * m * m * n + 2 * m ** 3)
+        if sum(t for _, t in done) > target_s:
+            break
+    secs = sum(t for _, t in done)
+    shapes = [f"{w.shapes[i][0]}x{w.shapes[i][1]}" for i, _ in done]
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": secs, "matrices_per_s": len(done) / secs,
+            "sample": f"{len(done)} matrices of the workload ({', '.join(shapes)}), one fp64 oracle "
+                      f"step each (numpy, BLAS threads={cores}); input generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-phase-timing", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU Muon step "
+              "(the multi-GPU sharding is a design note, not implemented); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import matrix_aware_optimizer_libmuon_amd as muon
+    from matrix_aware_optimizer_libmuon_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    muon._lib.load()          # fails loudly when libmuon.so is missing
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.key}: {w.name}; {w.n_mats} matrices, {w.elements() / 1e9:.3f} G elements")
+
+    t0 = time.perf_counter()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + w.key)
+    params, grads, moms = [], [], []
+    for i in range(w.n_mats):
+        p, g, m = W.device_inputs(w, i, dev, gen)
+        params.append(p)
+        grads.append(g)
+        moms.append(m)
+    ws = muon.alloc_workspace(w.shapes, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs on device in {time.perf_counter() - t0:.1f} s; workspace "
+        f"{ws.numel() / 2**30:.2f} GiB; HBM in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(lr=w.lr, mu=w.mu, wd=w.wd, ns_steps=w.ns_steps, coeffs=QUINTIC,
+              rms_scale=w.rms_mode, eps=w.eps, workspace=ws, stream=stream)
+
+    for k in range(args.warmup):
+        muon.muon_step(params, grads, moms, **kw)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {k + 1}/{args.warmup} done")
+
+    if not args.no_phase_timing:
+        muon.timing_enable(True)
+        muon.timing_read()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        muon.muon_step(params, grads, moms, **kw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    phases = muon.timing_read() if not args.no_phase_timing else None
+    muon.timing_enable(False)
+    ms_per_step = elapsed * 1e3 / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
+
+    flops_step = w.ns_flops()
+    value = flops_step / (ms_per_step / 1e3) / 1e12
+    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded device draws of the workload's laws)",
+           "config": {"workload": w.name, "n_matrices": w.n_mats,
+                      "shapes": sorted({f"{r}x{c}" for r, c in w.shapes}),
+                      "grad_dtype": w.grad_dtype, "ns_steps": w.ns_steps,
+                      "coeffs": list(QUINTIC), "lr": w.lr, "mu": w.mu, "wd": w.wd,
+                      "eps": w.eps, "rms_scale": w.rms_mode},
+           "matrices_per_s": w.n_mats / (ms_per_step / 1e3),
+           "frac_of_bf16_peak": value / BF16_PEAK_TFLOPS,
+           "nominal_ns_flops_per_step": flops_step}
+
+    if phases is not None:
+        work = phase_work(w)
+        per = {}
+        for name, rec in phases.items():
+            n = rec["launches"]
+            if n == 0:
+                continue
+            avg_ms = rec["ms"] / n
+            kind, amount = work[name]
+            if kind == "mfma":
+                achieved = amount / (avg_ms / 1e3) / 1e12
+                per[name] = {"launches_per_step": n / args.steps, "avg_launch_ms": avg_ms,
+                             "bound": "mfma", "achieved": achieved, "unit": "TFLOP/s",
+                             "peak": BF16_PEAK_TFLOPS, "frac": achieved / BF16_PEAK_TFLOPS,
+                             "algorithmic_per_launch": amount}
+            else:
+                achieved = amount / (avg_ms / 1e3) / 1e9
+                per[name] = {"launches_per_step": n / args.steps, "avg_launch_ms": avg_ms,
+                             "bound": "hbm", "achieved": achieved, "unit": "GB/s",
+                             "peak": HBM_PEAK_GBS, "frac": achieved / HBM_PEAK_GBS,
+                             "algorithmic_per_launch": amount}
+        ns_ms = sum(phases[k]["ms"] for k in ("gram", "gram2_epilogue", "x_update")) / args.steps
+        out["ns_ms_per_step"] = ns_ms
+        out["ns_tflops"] = flops_step / (ns_ms / 1e3) / 1e12
+        out["ns_frac_of_bf16_peak"] = out["ns_tflops"] / BF16_PEAK_TFLOPS
+        out["phases"] = per
+        dom = max(per, key=lambda k: per[k]["avg_launch_ms"] * per[k]["launches_per_step"])
+        d = per[dom]
+        out["roofline"] = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
+                           "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
+                           "traffic": None}
+
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * 2**30) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log(f"[bench] copy calibration: {n * 4 / 2**30:.2f} GiB copied")
+
+    del params, grads, moms, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

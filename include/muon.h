@@ -1,0 +1,194 @@
+/*
+ * libmuon -- the Muon optimizer step for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; no C++ or framework types cross it.
+ * All device memory (parameters, gradients, momentum buffers, outputs and the
+ * workspace) is owned by the caller.  The library launches work on the
+ * caller's HIP stream and never waits for it, except where a function below
+ * says so.
+ *
+ * What one step computes, for every 2-D matrix in the list (pages cited by
+ * title and section):
+ *   1. momentum, EMA form:        M <- mu*M + (1-mu)*G
+ *        ("Muon optimizer: matrix-aware LLM", airosetta.com, Muon.step loop;
+ *         "Muon meets Mamba", wmrh.cn, section 4.2 _step_muon)
+ *   2. Frobenius normalisation:   X0 = bf16(M / (||M||_F + eps))
+ *        (airosetta.com, newtonschulz5; "AdamW vs Muon", adg.csdn.net,
+ *         section "1. Preprocessing")
+ *   3. short side: when rows > cols the iteration works on the transpose
+ *        (airosetta.com, newtonschulz5).  Done by logical layout, never by a
+ *        copy.
+ *   4. ns_steps Newton-Schulz iterations, step k with (a_k, b_k, c_k):
+ *        A = X X^T ; B = b_k A + c_k A A ; X <- a_k X + B X
+ *        (airosetta.com newtonschulz5 loop; adg.csdn.net section
+ *         "2. Newton-Schulz iteration"; the hybrid schedule of section
+ *         "3. DeepSeek-V4 hybrid schedule" is a per-step coefficient list)
+ *      X, A and B are held in bf16 (the pages cast to bf16); every product is
+ *      accumulated in fp32 and rounded to bf16 once, to nearest-even.
+ *   5. decayed, scaled update:    p <- p*(1 - lr*wd) - lr*s*O
+ *        (wmrh.cn section 4.2; adg.csdn.net section "3. Scaling and update")
+ *      s = 1, or sqrt(max(1, rows/cols)) under MUON_SCALE_SQRT_MAX1 (the
+ *      csdn page asks for an RMS rescale by matrix size without a formula;
+ *      this is the reading taken), or the per-matrix `scale` when > 0.
+ *
+ * Error behaviour: every function returns MUON_OK (0) or a negative status.
+ * Argument errors are found on the host before anything is launched; nothing
+ * is modified then.  Kernel faults are asynchronous and surface at the
+ * caller's next synchronisation.  muon_status_string() describes a status;
+ * after MUON_EHIP it includes the HIP error text of the calling thread's last
+ * failure.
+ *
+ * Thread safety: calls may come from several host threads; two calls that
+ * run concurrently must use different workspaces.
+ */
+#ifndef LIBMUON_MUON_H
+#define LIBMUON_MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MUON_OK          0
+#define MUON_EINVAL     -1   /* bad argument (shape, pointer, count, value)   */
+#define MUON_EWORKSPACE -2   /* workspace missing, too small or misaligned    */
+#define MUON_EHIP       -3   /* a HIP runtime call or kernel launch failed    */
+#define MUON_EALIAS     -4   /* param / grad / momentum ranges overlap        */
+
+/* ---- element types ----------------------------------------------------- */
+#define MUON_F32  0
+#define MUON_BF16 1
+
+/* ---- RMS scale modes (call level) -------------------------------------- */
+#define MUON_SCALE_NONE        0   /* s = 1                                  */
+#define MUON_SCALE_SQRT_MAX1   1   /* s = sqrt(max(1, rows / cols))          */
+
+/* One matrix of a muon_step call.
+ *   param     fp32, rows x cols, row-major, contiguous; updated in place.
+ *   grad      rows x cols, row-major, contiguous, element type grad_dtype
+ *             (MUON_F32 or MUON_BF16).  NULL: the matrix is skipped entirely
+ *             (no momentum update, no decay), as the pages' optimizer skips
+ *             parameters without a gradient.
+ *   momentum  fp32, rows x cols, row-major, contiguous; updated in place.
+ *             The caller zero-initialises it before the first step.
+ *   rows, cols  >= 1 and <= MUON_MAX_DIM.  Only 2-D matrices are accepted;
+ *             routing 1-D parameters, embeddings and heads elsewhere is the
+ *             caller's job.
+ *   scale     per-matrix update scale s when > 0; otherwise the call's
+ *             rms_scale_mode decides.
+ * param, grad and momentum must be 4-byte aligned (16-byte alignment and
+ * cols % 8 == 0 select the vectorised path) and must not overlap each other
+ * or any other matrix's param / momentum. */
+typedef struct {
+  float*       param;
+  const void*  grad;
+  float*       momentum;
+  int64_t      rows;
+  int64_t      cols;
+  int32_t      grad_dtype;
+  float        scale;
+} muon_matrix_t;
+
+/* Coefficients of one Newton-Schulz iteration X <- a X + (b A + c A^2) X. */
+typedef struct { float a, b, c; } muon_ns_coeff_t;
+
+#define MUON_MAX_DIM      (1 << 20)
+#define MUON_MAX_NS_STEPS 64
+
+/* Bytes of device workspace a muon_step (or muon_orthogonalize) call over
+ * these shapes needs.  Depends only on the shapes (grad == NULL entries are
+ * counted too, so one workspace serves every call over the same list).
+ * Returns 0 when the list is invalid or empty. */
+size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n_mats);
+
+/* One Muon step over a list of matrices, as grouped launches: one launch per
+ * phase covers every matrix (3 + 3 * ns_steps launches in all), whatever
+ * their number and shapes.
+ *   lr, mu, wd   learning rate, momentum, decoupled weight decay (finite).
+ *   ns_steps     0 .. MUON_MAX_NS_STEPS Newton-Schulz iterations.
+ *   coeffs       n_coeffs triples: 1 (used for every step) or ns_steps (one
+ *                per step).  May be NULL only when ns_steps == 0.
+ *   rms_scale_mode  MUON_SCALE_NONE or MUON_SCALE_SQRT_MAX1.
+ *   eps          >= 0, added to ||M||_F before dividing.
+ *   workspace    device memory of at least muon_workspace_bytes(mats,
+ *                n_mats) bytes, 256-byte aligned.  Its contents on entry do
+ *                not matter; on return (once the stream reaches that point)
+ *                it holds every intermediate, see muon_workspace_view().
+ *   stream       HIP stream all work is queued on (0: the null stream).
+ * The matrix list itself is read during the call only. */
+int muon_step(const muon_matrix_t* mats, int64_t n_mats,
+              float lr, float mu, float wd, int ns_steps,
+              const muon_ns_coeff_t* coeffs, int n_coeffs,
+              int rms_scale_mode, float eps,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Orthogonalisation alone: out = NS(in) with the same normalisation,
+ * short-side rule and bf16 iteration as muon_step, for a list of matrices.
+ * The Newton-Schulz routine of the airosetta.com article (newtonschulz5) as a
+ * standalone call.
+ *   in       rows x cols, row-major, contiguous, type in_dtype (MUON_F32 or
+ *            MUON_BF16); read only.
+ *   out      bf16 (raw 16-bit patterns), rows x cols, row-major, contiguous;
+ *            written.  Must not overlap `in`.
+ * The workspace is sized by muon_workspace_bytes() over the same shapes
+ * (build the muon_matrix_t list with any grad pointer). */
+typedef struct {
+  const void*  in;
+  void*        out;
+  int64_t      rows;
+  int64_t      cols;
+  int32_t      in_dtype;
+} muon_ortho_t;
+
+int muon_orthogonalize(const muon_ortho_t* mats, int64_t n_mats, int ns_steps,
+                       const muon_ns_coeff_t* coeffs, int n_coeffs, float eps,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Where matrix `index`'s intermediates live in the workspace after a call
+ * over the same shapes (byte offsets from the workspace base).  Each bf16
+ * buffer is zero-padded: X buffers are rows_pad x cols_pad in the stored
+ * (rows x cols) orientation, A and B are m_pad x m_pad with m the short side.
+ *   x_off[0]  X0 and every even iterate; x_off[1] the odd iterates.
+ *   o_off     the final iterate O for `ns_steps` iterations.
+ *   nrm2_off  one double: sum of squares of M (of `in` for orthogonalize).
+ * Host-only; launches nothing.  For tests and diagnostics. */
+typedef struct {
+  size_t  x_off[2];
+  size_t  a_off;
+  size_t  b_off;
+  size_t  o_off;
+  size_t  nrm2_off;
+  int64_t rows_pad;
+  int64_t cols_pad;
+  int64_t m_pad;
+  int32_t transposed;   /* 1 when rows > cols: the iteration runs on X^T */
+  int32_t tile;         /* padding granule of this matrix                 */
+} muon_workspace_view_t;
+
+int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index,
+                        int ns_steps, muon_workspace_view_t* view);
+
+/* Phase timing with HIP events, for benchmarks.  When enabled, every launch
+ * is bracketed by a pair of events on the call's stream.  muon_timing_read()
+ * waits for the recorded events, returns the summed milliseconds and launch
+ * counts per phase (MUON_PHASES entries each; either pointer may be NULL) and
+ * clears the record.  Phases: momentum+norm, normalise+cast, Gram X X^T,
+ * Gram A A with the b A + c A^2 epilogue, X update, apply (or export). */
+#define MUON_PHASES 6
+int muon_timing_enable(int on);
+int muon_timing_read(double* ms, int64_t* launches);
+
+/* Static text for a status code (with HIP detail after MUON_EHIP). */
+const char* muon_status_string(int status);
+
+/* Library version, e.g. "libmuon 0.1 gfx950". */
+const char* muon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMUON_MUON_H */

@@ -1,0 +1,200 @@
+"""libmuon for MI355X: the Muon optimizer step as hand-written gfx950 kernels
+behind a C ABI (include/muon.h).  This module only marshals arguments: every
+step of the computation runs in libmuon.so.  PyTorch supplies device memory
+and the stream.
+
+    import torch
+    import matrix_aware_optimizer_libmuon_amd as muon
+    ws = muon.alloc_workspace([p.shape for p in params], device="cuda")
+    muon.muon_step(params, grads, moms, lr=0.02, mu=0.95, wd=0.01, workspace=ws)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Iterable, Sequence
+
+from . import _lib
+from ._lib import (MUON_BF16, MUON_EALIAS, MUON_EHIP, MUON_EINVAL, MUON_EWORKSPACE,  # noqa: F401
+                   MUON_F32, MUON_OK, MUON_SCALE_NONE, MUON_SCALE_SQRT_MAX1, PHASE_NAMES,
+                   LibMuonError, MuonCoeff, MuonMatrix, MuonOrtho, MuonWorkspaceView,
+                   status_string)
+
+# Quintic Newton-Schulz coefficients (a, b, c) of the newtonschulz5 routine in
+# "Muon optimizer: matrix-aware LLM" (airosetta.com, implementation section).
+QUINTIC = (3.4445, -4.7750, 2.0315)
+# "AdamW vs Muon" (adg.csdn.net), section "3. DeepSeek-V4 hybrid schedule":
+# 8 quintic steps then 2 steps of (2, -1.5, 0.5).
+HYBRID = [QUINTIC] * 8 + [(2.0, -1.5, 0.5)] * 2
+
+
+def version() -> str:
+    return _lib.load().muon_version().decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MUON_F32
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _check_2d(t, name: str, dtype=None):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _coeff_array(coeffs, ns_steps: int):
+    if coeffs is None:
+        coeffs = QUINTIC
+    if len(coeffs) == 3 and not isinstance(coeffs[0], (tuple, list)):
+        coeffs = [tuple(coeffs)]
+    coeffs = [tuple(float(v) for v in c) for c in coeffs]
+    arr = (MuonCoeff * max(1, len(coeffs)))(*[MuonCoeff(*c) for c in coeffs])
+    return arr, len(coeffs)
+
+
+def _shapes_array(shapes: Sequence) -> ctypes.Array:
+    arr = (MuonMatrix * max(1, len(shapes)))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i].rows = int(r)
+        arr[i].cols = int(c)
+    return arr
+
+
+def workspace_bytes(shapes: Sequence) -> int:
+    """Workspace bytes for a list of (rows, cols)."""
+    shapes = [tuple(int(v) for v in s) for s in shapes]
+    if not shapes:
+        return 0
+    n = _lib.load().muon_workspace_bytes(_shapes_array(shapes), len(shapes))
+    if n == 0:
+        raise ValueError("invalid shape list")
+    return int(n)
+
+
+def alloc_workspace(shapes: Sequence, device="cuda"):
+    """A uint8 device tensor big enough for ``shapes`` (256-byte aligned)."""
+    torch = _torch()
+    n = workspace_bytes(shapes)
+    ws = torch.empty(max(n, 256) + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + max(n, 256)]
+
+
+def workspace_view(shapes: Sequence, index: int, ns_steps: int) -> dict:
+    """Byte offsets of matrix ``index``'s intermediates in the workspace."""
+    shapes = [tuple(int(v) for v in s) for s in shapes]
+    v = MuonWorkspaceView()
+    _lib.check(_lib.load().muon_workspace_view(_shapes_array(shapes), len(shapes), int(index),
+                                               int(ns_steps), ctypes.byref(v)),
+               "muon_workspace_view")
+    return {"x_off": (v.x_off[0], v.x_off[1]), "a_off": v.a_off, "b_off": v.b_off,
+            "o_off": v.o_off, "nrm2_off": v.nrm2_off, "rows_pad": v.rows_pad,
+            "cols_pad": v.cols_pad, "m_pad": v.m_pad, "transposed": bool(v.transposed),
+            "tile": v.tile}
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 0.02,
+              mu: float = 0.95, wd: float = 0.0, ns_steps: int = 5, coeffs=QUINTIC,
+              rms_scale: str | None = None, eps: float = 1e-7, scales: Sequence | None = None,
+              workspace=None, stream=None):
+    """One Muon step over lists of 2-D fp32 params, grads (fp32 or bf16, or
+    None to skip) and fp32 momentum buffers, all on one GPU.  Updates params
+    and momenta in place on ``stream`` (default: the current stream) and
+    returns the workspace tensor used."""
+    torch = _torch()
+    n = len(params)
+    if len(grads) != n or len(moms) != n:
+        raise ValueError("params, grads and moms must have the same length")
+    if rms_scale not in (None, "none", "sqrt_max1"):
+        raise ValueError(f"unknown rms_scale {rms_scale!r}")
+    mode = MUON_SCALE_SQRT_MAX1 if rms_scale == "sqrt_max1" else MUON_SCALE_NONE
+    arr = (MuonMatrix * max(1, n))()
+    device = params[0].device if n else torch.device("cuda")
+    for i, (p, g, m) in enumerate(zip(params, grads, moms)):
+        _check_2d(p, f"params[{i}]", torch.float32)
+        _check_2d(m, f"moms[{i}]", torch.float32)
+        if m.shape != p.shape:
+            raise ValueError(f"moms[{i}] shape {tuple(m.shape)} != param shape {tuple(p.shape)}")
+        arr[i].param = p.data_ptr()
+        arr[i].momentum = m.data_ptr()
+        arr[i].rows, arr[i].cols = p.shape
+        arr[i].scale = float(scales[i]) if scales is not None and scales[i] is not None else 0.0
+        if g is not None:
+            _check_2d(g, f"grads[{i}]")
+            if g.shape != p.shape:
+                raise ValueError(f"grads[{i}] shape {tuple(g.shape)} != param shape {tuple(p.shape)}")
+            arr[i].grad = g.data_ptr()
+            arr[i].grad_dtype = _dtype_code(g)
+    if workspace is None:
+        workspace = alloc_workspace([tuple(p.shape) for p in params], device)
+    carr, nc = _coeff_array(coeffs, ns_steps)
+    st = _lib.load().muon_step(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
+                               mode, float(eps), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel() * workspace.element_size(),
+                               _stream_handle(stream, device))
+    _lib.check(st, "muon_step")
+    return workspace
+
+
+def orthogonalize(inputs: Sequence, outputs: Sequence | None = None, *, ns_steps: int = 5,
+                  coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None):
+    """out_i = NS(in_i) in bf16 for a list of 2-D fp32/bf16 GPU tensors.
+    Returns the list of bf16 outputs (allocated when not given)."""
+    torch = _torch()
+    n = len(inputs)
+    device = inputs[0].device if n else torch.device("cuda")
+    if outputs is None:
+        outputs = [torch.empty(t.shape, dtype=torch.bfloat16, device=t.device) for t in inputs]
+    arr = (MuonOrtho * max(1, n))()
+    for i, (x, y) in enumerate(zip(inputs, outputs)):
+        _check_2d(x, f"inputs[{i}]")
+        _check_2d(y, f"outputs[{i}]", torch.bfloat16)
+        if y.shape != x.shape:
+            raise ValueError(f"outputs[{i}] shape mismatch")
+        arr[i].inp = x.data_ptr()
+        arr[i].out = y.data_ptr()
+        arr[i].rows, arr[i].cols = x.shape
+        arr[i].in_dtype = _dtype_code(x)
+    if workspace is None:
+        workspace = alloc_workspace([tuple(t.shape) for t in inputs], device)
+    carr, nc = _coeff_array(coeffs, ns_steps)
+    st = _lib.load().muon_orthogonalize(arr, n, int(ns_steps), carr, nc, float(eps),
+                                        ctypes.c_void_p(workspace.data_ptr()),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream, device))
+    _lib.check(st, "muon_orthogonalize")
+    return outputs
+
+
+def timing_enable(on: bool = True) -> None:
+    _lib.check(_lib.load().muon_timing_enable(1 if on else 0), "muon_timing_enable")
+
+
+def timing_read() -> dict:
+    """Per-phase summed milliseconds and launch counts since the last read
+    (waits for the recorded events)."""
+    ms = (ctypes.c_double * _lib.MUON_PHASES)()
+    cnt = (ctypes.c_int64 * _lib.MUON_PHASES)()
+    _lib.check(_lib.load().muon_timing_read(ms, cnt), "muon_timing_read")
+    return {name: {"ms": ms[k], "launches": cnt[k]} for k, name in enumerate(PHASE_NAMES)}

@@ -1,0 +1,497 @@
+// Host side of libmuon: argument checks, workspace planning, the device
+// descriptor table and the grouped launch sequence.  The C ABI is declared
+// in include/muon.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_hip_detail;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// workspace plan (a pure function of the shapes)
+//
+//   [ table: MatDesc[n] | 4 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
+//   then, per matrix (all n, skipped ones included):
+//   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | B ] m_pad x m_pad bf16 each
+// ---------------------------------------------------------------------------
+struct MatPlan {
+  int64_t rows, cols, rows_pad, cols_pad, m_pad, n_pad;
+  bool tall;
+  size_t x_off[2], a_off, b_off;
+};
+
+struct Plan {
+  int64_t n = 0;
+  size_t desc_off = 0, prefix_off[4] = {0, 0, 0, 0}, nrm2_off = 0, table_bytes = 0;
+  size_t total = 0;
+  std::vector<MatPlan> mats;
+};
+
+bool shape_ok(int64_t r, int64_t c) { return r >= 1 && c >= 1 && r <= MUON_MAX_DIM && c <= MUON_MAX_DIM; }
+
+template <class GetShape>
+bool make_plan(int64_t n, GetShape shape, Plan& plan) {
+  plan = Plan();
+  plan.n = n;
+  plan.desc_off = 0;
+  size_t off = static_cast<size_t>(n) * sizeof(MatDesc);
+  for (int k = 0; k < 4; ++k) {
+    plan.prefix_off[k] = off;
+    off += static_cast<size_t>(n + 1) * sizeof(int64_t);
+  }
+  plan.nrm2_off = off;
+  off += static_cast<size_t>(n) * sizeof(double);
+  plan.table_bytes = align_up(off, kAlign);
+  off = plan.table_bytes;
+  plan.mats.resize(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t r, c;
+    shape(i, r, c);
+    if (!shape_ok(r, c)) return false;
+    MatPlan& m = plan.mats[static_cast<size_t>(i)];
+    m.rows = r;
+    m.cols = c;
+    m.rows_pad = round_up(r, kTile);
+    m.cols_pad = round_up(c, kTile);
+    m.tall = r > c;
+    m.m_pad = m.tall ? m.cols_pad : m.rows_pad;
+    m.n_pad = m.tall ? m.rows_pad : m.cols_pad;
+    const size_t xb = static_cast<size_t>(m.rows_pad) * static_cast<size_t>(m.cols_pad) * 2;
+    const size_t ab = static_cast<size_t>(m.m_pad) * static_cast<size_t>(m.m_pad) * 2;
+    m.x_off[0] = off;
+    off = align_up(off + xb, kAlign);
+    m.x_off[1] = off;
+    off = align_up(off + xb, kAlign);
+    m.a_off = off;
+    off = align_up(off + ab, kAlign);
+    m.b_off = off;
+    off = align_up(off + ab, kAlign);
+  }
+  plan.total = off;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// pinned staging ring for the descriptor upload (per device)
+// ---------------------------------------------------------------------------
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+struct DeviceState {
+  Slot slots[4];
+  int next = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+
+// timing
+struct TimingRec {
+  int phase;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<TimingRec> g_trecs;
+std::vector<hipEvent_t> g_evpool;
+
+hipEvent_t pool_event() {
+  if (!g_evpool.empty()) {
+    hipEvent_t e = g_evpool.back();
+    g_evpool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_hip_detail = std::string(what) + ": " + hipGetErrorString(e);
+  return MUON_EHIP;
+}
+
+int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  Slot& s = st.slots[st.next];
+  st.next = (st.next + 1) % 4;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);  // the copy that last used this slot has finished
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
+    s.pending = false;
+  }
+  if (!s.ev) {
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
+  }
+  if (s.cap < bytes) {
+    if (s.host) hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src, bytes);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (descriptor table)");
+  e = hipEventRecord(s.ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
+  s.pending = true;
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launch sequence
+// ---------------------------------------------------------------------------
+template <class F>
+int timed(int phase, hipStream_t stream, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    timing = g_timing;
+    if (timing) {
+      a = pool_event();
+      b = pool_event();
+      if (!a || !b) return hip_fail(hipErrorOutOfMemory, "hipEventCreate (timing)");
+    }
+  }
+  if (timing) {
+    hipError_t e = hipEventRecord(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
+  }
+  const int err = launch();
+  if (err != hipSuccess) return hip_fail(static_cast<hipError_t>(err), "kernel launch");
+  if (timing) {
+    hipError_t e = hipEventRecord(b, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (timing)");
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_trecs.push_back({phase, a, b});
+  }
+  return MUON_OK;
+}
+
+struct Table {
+  std::vector<unsigned char> bytes;
+  int n_active = 0;
+  int64_t units[4] = {0, 0, 0, 0};  // flat chunks, padded chunks, sym tiles, full tiles
+};
+
+bool finite(float x) { return std::isfinite(x); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, float eps) {
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS) return MUON_EINVAL;
+  if (ns_steps > 0) {
+    if (!coeffs || !(n_coeffs == 1 || n_coeffs == ns_steps)) return MUON_EINVAL;
+    for (int k = 0; k < n_coeffs; ++k)
+      if (!finite(coeffs[k].a) || !finite(coeffs[k].b) || !finite(coeffs[k].c)) return MUON_EINVAL;
+  }
+  if (!(eps >= 0.0f) || !finite(eps)) return MUON_EINVAL;
+  return MUON_OK;
+}
+
+// Overlap check over [begin, end) ranges (n log n).
+bool any_overlap(std::vector<std::pair<uintptr_t, uintptr_t>>& r) {
+  std::sort(r.begin(), r.end());
+  for (size_t k = 1; k < r.size(); ++k)
+    if (r[k].first < r[k - 1].second) return true;
+  return false;
+}
+
+// Fill the descriptor table for the active matrices.
+template <class Fill>
+void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) {
+  const size_t n = static_cast<size_t>(plan.n);
+  t.bytes.assign(plan.table_bytes, 0);
+  t.n_active = n_active;
+  MatDesc* desc = reinterpret_cast<MatDesc*>(t.bytes.data() + plan.desc_off);
+  int64_t* pre[4];
+  for (int k = 0; k < 4; ++k) pre[k] = reinterpret_cast<int64_t*>(t.bytes.data() + plan.prefix_off[k]);
+  int64_t acc[4] = {0, 0, 0, 0};
+  int a = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const MatPlan& m = plan.mats[i];
+    MatDesc d;
+    std::memset(&d, 0, sizeof(d));
+    if (!fill(i, d)) continue;
+    d.x[0] = reinterpret_cast<uint16_t*>(ws + m.x_off[0]);
+    d.x[1] = reinterpret_cast<uint16_t*>(ws + m.x_off[1]);
+    d.a = reinterpret_cast<uint16_t*>(ws + m.a_off);
+    d.b = reinterpret_cast<uint16_t*>(ws + m.b_off);
+    d.nrm2 = reinterpret_cast<double*>(ws + plan.nrm2_off) + i;
+    d.rows = m.rows;
+    d.cols = m.cols;
+    d.rows_pad = static_cast<int32_t>(m.rows_pad);
+    d.cols_pad = static_cast<int32_t>(m.cols_pad);
+    d.m_pad = static_cast<int32_t>(m.m_pad);
+    d.n_pad = static_cast<int32_t>(m.n_pad);
+    if (m.tall) d.flags |= kFlagTall;
+    desc[a] = d;
+    const int64_t flat = m.rows * m.cols;
+    const int64_t padded = m.rows_pad * m.cols_pad;
+    const int64_t t_side = m.m_pad / kTile;
+    const int64_t units[4] = {(flat + kChunk - 1) / kChunk, (padded + kChunk - 1) / kChunk,
+                              t_side * (t_side + 1) / 2, (m.rows_pad / kTile) * (m.cols_pad / kTile)};
+    for (int k = 0; k < 4; ++k) {
+      pre[k][a] = acc[k];
+      acc[k] += units[k];
+    }
+    ++a;
+  }
+  for (int k = 0; k < 4; ++k) {
+    pre[k][a] = acc[k];
+    t.units[k] = acc[k];
+  }
+}
+
+int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float lr, float mu,
+                 float wd, int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, float eps,
+                 hipStream_t stream) {
+  int rc = upload_table(t.bytes.data(), t.bytes.size(), ws, stream);
+  if (rc != MUON_OK) return rc;
+  if (t.n_active == 0) return MUON_OK;
+  const MatDesc* d = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
+  const int64_t* pre[4];
+  for (int k = 0; k < 4; ++k) pre[k] = reinterpret_cast<const int64_t*>(ws + plan.prefix_off[k]);
+  const int n = t.n_active;
+  void* s = static_cast<void*>(stream);
+  rc = timed(kPhaseMomentumNorm, stream, [&] {
+    return launch_momentum_norm(d, pre[0], n, t.units[0], mu, ortho ? 1 : 0, s);
+  });
+  if (rc) return rc;
+  rc = timed(kPhaseNormalize, stream, [&] { return launch_normalize(d, pre[1], n, t.units[1], eps, s); });
+  if (rc) return rc;
+  for (int k = 0; k < ns_steps; ++k) {
+    const muon_ns_coeff_t& c = coeffs[n_coeffs == 1 ? 0 : k];
+    const int parity = k & 1;
+    rc = timed(kPhaseGram, stream, [&] { return launch_gram(d, pre[2], n, t.units[2], parity, s); });
+    if (rc) return rc;
+    rc = timed(kPhaseGram2, stream, [&] { return launch_gram2(d, pre[2], n, t.units[2], c.b, c.c, s); });
+    if (rc) return rc;
+    rc = timed(kPhaseXUpdate, stream, [&] { return launch_xupdate(d, pre[3], n, t.units[3], parity, c.a, s); });
+    if (rc) return rc;
+  }
+  rc = timed(kPhaseApply, stream, [&] {
+    return launch_apply(d, pre[0], n, t.units[0], ns_steps & 1, lr, wd, ortho ? 1 : 0, s);
+  });
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n_mats) {
+  if (n_mats <= 0 || !mats) return 0;
+  Plan plan;
+  if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
+    return 0;
+  return plan.total;
+}
+
+int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd, int ns_steps,
+              const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_mats < 0 || (n_mats > 0 && !mats)) return MUON_EINVAL;
+  if (n_mats > (int64_t(1) << 24)) return MUON_EINVAL;
+  if (!finite(lr) || !finite(mu) || !finite(wd)) return MUON_EINVAL;
+  if (rms_scale_mode != MUON_SCALE_NONE && rms_scale_mode != MUON_SCALE_SQRT_MAX1) return MUON_EINVAL;
+  int rc = check_common(ns_steps, coeffs, n_coeffs, eps);
+  if (rc) return rc;
+  if (n_mats == 0) return MUON_OK;
+  std::vector<std::pair<uintptr_t, uintptr_t>> ranges;
+  int n_active = 0;
+  for (int64_t i = 0; i < n_mats; ++i) {
+    const muon_matrix_t& m = mats[i];
+    if (!shape_ok(m.rows, m.cols)) return MUON_EINVAL;
+    if (!m.grad) continue;
+    if (!m.param || !m.momentum) return MUON_EINVAL;
+    if (m.grad_dtype != MUON_F32 && m.grad_dtype != MUON_BF16) return MUON_EINVAL;
+    if (!(m.scale <= 0.0f || finite(m.scale))) return MUON_EINVAL;
+    if (std::isnan(m.scale)) return MUON_EINVAL;
+    const size_t gsz = m.grad_dtype == MUON_BF16 ? 2 : 4;
+    if (!aligned(m.param, 4) || !aligned(m.momentum, 4) || !aligned(m.grad, gsz)) return MUON_EINVAL;
+    const size_t el = static_cast<size_t>(m.rows) * static_cast<size_t>(m.cols);
+    ranges.push_back({reinterpret_cast<uintptr_t>(m.param), reinterpret_cast<uintptr_t>(m.param) + el * 4});
+    ranges.push_back({reinterpret_cast<uintptr_t>(m.momentum), reinterpret_cast<uintptr_t>(m.momentum) + el * 4});
+    ranges.push_back({reinterpret_cast<uintptr_t>(m.grad), reinterpret_cast<uintptr_t>(m.grad) + el * gsz});
+    ++n_active;
+  }
+  if (any_overlap(ranges)) return MUON_EALIAS;
+  Plan plan;
+  if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
+    return MUON_EINVAL;
+  if (!workspace || workspace_bytes < plan.total || !aligned(workspace, kAlign)) return MUON_EWORKSPACE;
+  if (n_active == 0) return MUON_OK;
+  char* ws = static_cast<char*>(workspace);
+  Table t;
+  build_table(plan, ws, n_active, [&](size_t i, MatDesc& d) {
+    const muon_matrix_t& m = mats[i];
+    if (!m.grad) return false;
+    d.param = m.param;
+    d.grad = m.grad;
+    d.mom = m.momentum;
+    const bool bf = m.grad_dtype == MUON_BF16;
+    if (bf) d.flags |= kFlagGradBf16;
+    const int64_t el = m.rows * m.cols;
+    if (el % 8 == 0 && aligned(m.param, 16) && aligned(m.momentum, 16) && aligned(m.grad, 16))
+      d.flags |= kFlagVecFlat;
+    if ((d.flags & kFlagVecFlat) && m.cols % 8 == 0) d.flags |= kFlagVecRows;
+    if (m.scale > 0.0f) d.scale = m.scale;
+    else if (rms_scale_mode == MUON_SCALE_SQRT_MAX1)
+      d.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(m.rows) / static_cast<double>(m.cols))));
+    else d.scale = 1.0f;
+    return true;
+  }, t);
+  return run_sequence(plan, t, ws, false, lr, mu, wd, ns_steps, coeffs, n_coeffs, eps, stream);
+}
+
+int muon_orthogonalize(const muon_ortho_t* mats, int64_t n_mats, int ns_steps,
+                       const muon_ns_coeff_t* coeffs, int n_coeffs, float eps, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (n_mats < 0 || (n_mats > 0 && !mats)) return MUON_EINVAL;
+  if (n_mats > (int64_t(1) << 24)) return MUON_EINVAL;
+  int rc = check_common(ns_steps, coeffs, n_coeffs, eps);
+  if (rc) return rc;
+  if (n_mats == 0) return MUON_OK;
+  std::vector<std::pair<uintptr_t, uintptr_t>> ranges;
+  for (int64_t i = 0; i < n_mats; ++i) {
+    const muon_ortho_t& m = mats[i];
+    if (!shape_ok(m.rows, m.cols)) return MUON_EINVAL;
+    if (!m.in || !m.out) return MUON_EINVAL;
+    if (m.in_dtype != MUON_F32 && m.in_dtype != MUON_BF16) return MUON_EINVAL;
+    const size_t isz = m.in_dtype == MUON_BF16 ? 2 : 4;
+    if (!aligned(m.in, isz) || !aligned(m.out, 2)) return MUON_EINVAL;
+    const size_t el = static_cast<size_t>(m.rows) * static_cast<size_t>(m.cols);
+    ranges.push_back({reinterpret_cast<uintptr_t>(m.out), reinterpret_cast<uintptr_t>(m.out) + el * 2});
+    ranges.push_back({reinterpret_cast<uintptr_t>(m.in), reinterpret_cast<uintptr_t>(m.in) + el * isz});
+  }
+  if (any_overlap(ranges)) return MUON_EALIAS;
+  Plan plan;
+  if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
+    return MUON_EINVAL;
+  if (!workspace || workspace_bytes < plan.total || !aligned(workspace, kAlign)) return MUON_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  Table t;
+  build_table(plan, ws, static_cast<int>(n_mats), [&](size_t i, MatDesc& d) {
+    const muon_ortho_t& m = mats[i];
+    d.grad = m.in;
+    d.out = static_cast<uint16_t*>(m.out);
+    if (m.in_dtype == MUON_BF16) d.flags |= kFlagGradBf16;
+    const int64_t el = m.rows * m.cols;
+    if (el % 8 == 0 && aligned(m.in, 16) && aligned(m.out, 16)) d.flags |= kFlagVecFlat;
+    if ((d.flags & kFlagVecFlat) && m.cols % 8 == 0) d.flags |= kFlagVecRows;
+    d.scale = 1.0f;
+    return true;
+  }, t);
+  return run_sequence(plan, t, ws, true, 0.f, 0.f, 0.f, ns_steps, coeffs, n_coeffs, eps, stream);
+}
+
+int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index, int ns_steps,
+                        muon_workspace_view_t* view) {
+  if (!mats || !view || n_mats <= 0 || index < 0 || index >= n_mats) return MUON_EINVAL;
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS) return MUON_EINVAL;
+  Plan plan;
+  if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
+    return MUON_EINVAL;
+  const MatPlan& m = plan.mats[static_cast<size_t>(index)];
+  view->x_off[0] = m.x_off[0];
+  view->x_off[1] = m.x_off[1];
+  view->a_off = m.a_off;
+  view->b_off = m.b_off;
+  view->o_off = m.x_off[ns_steps & 1];
+  view->nrm2_off = plan.nrm2_off + static_cast<size_t>(index) * sizeof(double);
+  view->rows_pad = m.rows_pad;
+  view->cols_pad = m.cols_pad;
+  view->m_pad = m.m_pad;
+  view->transposed = m.tall ? 1 : 0;
+  view->tile = kTile;
+  return MUON_OK;
+}
+
+int muon_timing_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_timing = on != 0;
+  return MUON_OK;
+}
+
+int muon_timing_read(double* ms, int64_t* launches) {
+  std::vector<TimingRec> recs;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    recs.swap(g_trecs);
+  }
+  double acc[MUON_PHASES] = {0};
+  int64_t cnt[MUON_PHASES] = {0};
+  int rc = MUON_OK;
+  for (const TimingRec& r : recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess && rc == MUON_OK) rc = hip_fail(e, "hipEventElapsedTime");
+    if (r.phase >= 0 && r.phase < MUON_PHASES) {
+      acc[r.phase] += t;
+      cnt[r.phase] += 1;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (const TimingRec& r : recs) {
+      g_evpool.push_back(r.a);
+      g_evpool.push_back(r.b);
+    }
+  }
+  for (int k = 0; k < MUON_PHASES; ++k) {
+    if (ms) ms[k] = acc[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return rc;
+}
+
+const char* muon_status_string(int status) {
+  static thread_local std::string s;
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_EINVAL: return "invalid argument";
+    case MUON_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case MUON_EALIAS: return "param / grad / momentum (or in / out) ranges overlap";
+    case MUON_EHIP:
+      s = "HIP error: " + g_hip_detail;
+      return s.c_str();
+    default: return "unknown status";
+  }
+}
+
+const char* muon_version(void) { return "libmuon 0.1 gfx950"; }
+
+}  // extern "C"

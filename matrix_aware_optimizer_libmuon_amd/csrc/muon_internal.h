@@ -1,0 +1,75 @@
+// Internal structures shared by the host dispatcher and the gfx950 kernels.
+//
+// Every call builds one device descriptor table (one MatDesc per active
+// matrix) plus, per phase, a prefix sum of that phase's work units (element
+// chunks or output tiles) per matrix.  Each phase is then ONE launch over the
+// sum of all matrices' units: a workgroup finds its matrix by binary search
+// in the prefix array.
+#pragma once
+#include <stdint.h>
+
+namespace muon {
+
+// Output tile of the Newton-Schulz GEMMs and padding granule of every bf16
+// workspace buffer.  All X / A / B buffers are zero-padded to multiples of
+// kTile in both dimensions, so the GEMM kernels never need bounds checks:
+// zero rows and columns of X keep producing exact zeros in A, B and X'.
+constexpr int kTile = 128;
+// Depth of one K step of the GEMM main loop.
+constexpr int kTileK = 64;
+// Elements handled by one workgroup of the elementwise phases.
+constexpr int kChunk = 16384;
+constexpr int kEwThreads = 256;
+constexpr int kGemmThreads = 256;
+
+enum Phase : int {
+  kPhaseMomentumNorm = 0,
+  kPhaseNormalize = 1,
+  kPhaseGram = 2,
+  kPhaseGram2 = 3,
+  kPhaseXUpdate = 4,
+  kPhaseApply = 5,
+  kNumPhases = 6
+};
+
+// flags of MatDesc
+enum : uint32_t {
+  kFlagTall = 1u,        // rows > cols: the iteration runs on the transpose
+  kFlagGradBf16 = 2u,    // grad / input is bf16 (else fp32)
+  kFlagVecFlat = 4u,     // param/grad/mom 16-byte aligned and rows*cols % 8 == 0
+  kFlagVecRows = 8u,     // additionally cols % 8 == 0 (row-wise 8-vectors)
+};
+
+// One matrix, as the kernels see it.  128 bytes.
+struct alignas(16) MatDesc {
+  float* param;          // fp32 rows x cols (muon_step) / unused (orthogonalize)
+  const void* grad;      // grad (muon_step) or input (orthogonalize)
+  float* mom;            // fp32 momentum (muon_step) / unused
+  uint16_t* out;         // orthogonalize: bf16 rows x cols output / unused
+  uint16_t* x[2];        // ping-pong bf16 X buffers, rows_pad x cols_pad
+  uint16_t* a;           // bf16 m_pad x m_pad Gram
+  uint16_t* b;           // bf16 m_pad x m_pad b A + c A A
+  double* nrm2;          // sum of squares of M
+  int64_t rows, cols;
+  int32_t rows_pad, cols_pad, m_pad, n_pad;
+  uint32_t flags;
+  float scale;           // update scale s
+  int32_t reserved[4];
+};
+static_assert(sizeof(MatDesc) == 128, "descriptor size");
+
+// kernel launchers (muon_kernels.hip); return hipError_t as int
+int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                         float mu, int norm_only, void* stream);
+int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                     float eps, void* stream);
+int launch_gram(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                void* stream);
+int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float b,
+                 float c, void* stream);
+int launch_xupdate(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                   float a, void* stream);
+int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                 float lr, float wd, int export_only, void* stream);
+
+}  // namespace muon

@@ -227,3 +227,70 @@ def iter_inputs(w: Workload, indices=None, step: int = 0, threads: int = 8,
             if nxt < len(indices):
                 futs[nxt] = ex.submit(matrix_inputs, w, indices[nxt], step, with_state)
             yield idx, futs.pop(j).result()
+
+
+def adhoc_inputs(rows: int, cols: int, grad_dtype: str, seed: int, grad_std: float = 1.0,
+                 mom_std: float = 0.0, param_std: float = 0.02) -> MatrixInputs:
+    """Seeded inputs of any shape (edge-case tests): N(0, grad_std) gradient
+    (rounded to bf16 when asked), N(0, mom_std) momentum, N(0, param_std)
+    parameter.  Seeds live in their own range (workload key 1000)."""
+    g = _normal(_rng(1000, seed, rows, cols, ROLE_GRAD), (rows, cols), grad_std)
+    bits = None
+    if grad_dtype == "bf16":
+        bits = f32_to_bf16_bits(g)
+        g = bf16_bits_to_f32(bits)
+    m = (_normal(_rng(1000, seed, rows, cols, ROLE_MOM), (rows, cols), mom_std)
+         if mom_std > 0 else np.zeros((rows, cols), dtype=np.float32))
+    p = _normal(_rng(1000, seed, rows, cols, ROLE_PARAM), (rows, cols), param_std)
+    return MatrixInputs(rows, cols, np.ascontiguousarray(g), bits, p, m)
+
+
+# --------------------------------------------------------------------------
+# device-side draws (benchmark inputs): the same laws as above, drawn by
+# torch's seeded device generator so that the 7.8 G-element workloads do not
+# spend minutes on the host.  Values differ from the host recipe (another
+# random stream); shapes, dtypes, laws and structure are the same.
+# --------------------------------------------------------------------------
+def device_inputs(w: Workload, idx: int, device, gen, step: int = 0):
+    """(param fp32, grad fp32/bf16, mom fp32) torch tensors for matrix idx."""
+    import torch
+    r, c = w.shapes[idx]
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    if w.key == 1:
+        g = randn(r, c)
+    elif w.key == 2:
+        g = randn(r, c).mul_(0.02)
+    elif w.key == 3:
+        g = randn(r, c).mul_(1e-3)
+        # rank-8 spike: orthonormal factors from a seeded host QR (tiny)
+        u, _ = np.linalg.qr(_rng(w.key, step, idx, ROLE_SPIKE_U).standard_normal((r, 8)))
+        v, _ = np.linalg.qr(_rng(w.key, step, idx, ROLE_SPIKE_V).standard_normal((c, 8)))
+        ut = torch.from_numpy(u.astype(np.float32)).to(device)
+        vt = torch.from_numpy(v.astype(np.float32)).to(device)
+        g.addmm_(ut, vt.t().contiguous(), alpha=float(1e-3 * np.sqrt(r * c)))
+    elif w.key == 4:
+        g = randn(r, c)
+    elif w.key == 5:
+        g = _student_t3(randn, r, c).mul_(1e-3)
+    else:
+        raise KeyError(w.key)
+    if w.grad_dtype == "bf16":
+        g = g.to(torch.bfloat16)
+    p = randn(r, c).mul_(0.02)
+    if w.key == 5:
+        m = _student_t3(randn, r, c).mul_(1e-3).to(torch.bfloat16).float().mul_(0.05)
+    else:
+        m = torch.zeros(r, c, device=device, dtype=torch.float32)
+    return p, g, m
+
+
+def _student_t3(randn, r, c):
+    """t with 3 degrees of freedom: Z / sqrt(chi2_3 / 3), chi2_3 a sum of
+    three squared standard normals."""
+    z = randn(r, c)
+    chi = randn(r, c).square_()
+    chi.add_(randn(r, c).square_()).add_(randn(r, c).square_())
+    return z.div_(chi.div_(3.0).sqrt_())

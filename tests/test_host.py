@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/muon.h declares, plans workspaces consistently, and
+rejects bad arguments before touching the device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import matrix_aware_optimizer_libmuon_amd as muon
+from matrix_aware_optimizer_libmuon_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from matrix_aware_optimizer_libmuon_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(muon_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert muon.version().startswith("libmuon")
+
+
+def test_struct_layouts_match_header(lib):
+    # sizes the C compiler gives the public structs (LP64)
+    assert ctypes.sizeof(muon.MuonMatrix) == 48
+    assert ctypes.sizeof(muon.MuonOrtho) == 40
+    assert ctypes.sizeof(muon.MuonCoeff) == 12
+    assert ctypes.sizeof(muon.MuonWorkspaceView) == 80
+
+
+def test_workspace_plan(lib):
+    shapes = [(256, 768), (1536, 80), (48, 1536), (1, 1), (300, 300)]
+    total = muon.workspace_bytes(shapes)
+    views = [muon.workspace_view(shapes, i, 5) for i in range(len(shapes))]
+    end = 0
+    for (r, c), v in zip(shapes, views):
+        t = v["tile"]
+        assert v["rows_pad"] == math.ceil(r / t) * t and v["cols_pad"] == math.ceil(c / t) * t
+        assert v["transposed"] == (r > c)
+        assert v["m_pad"] == (v["cols_pad"] if r > c else v["rows_pad"])
+        xb = v["rows_pad"] * v["cols_pad"] * 2
+        ab = v["m_pad"] ** 2 * 2
+        assert v["x_off"][0] % 256 == 0 and v["x_off"][0] >= end
+        assert v["x_off"][1] >= v["x_off"][0] + xb
+        assert v["a_off"] >= v["x_off"][1] + xb and v["b_off"] >= v["a_off"] + ab
+        assert v["o_off"] == v["x_off"][1]          # 5 iterations end in the odd buffer
+        end = v["b_off"] + ab
+    assert end <= total
+    assert muon.workspace_view(shapes, 0, 4)["o_off"] == views[0]["x_off"][0]
+    nrm = [v["nrm2_off"] for v in views]
+    assert all(b - a == 8 for a, b in zip(nrm, nrm[1:])) and nrm[-1] + 8 <= views[0]["x_off"][0]
+
+
+def test_workspace_rejects_bad_shapes(lib):
+    with pytest.raises(ValueError):
+        muon.workspace_bytes([(0, 5)])
+    with pytest.raises(ValueError):
+        muon.workspace_bytes([(5, (1 << 20) + 1)])
+    assert muon.workspace_bytes([]) == 0
+
+
+def _mats(specs):
+    arr = (muon.MuonMatrix * len(specs))()
+    for i, s in enumerate(specs):
+        for k, v in s.items():
+            setattr(arr[i], k, v)
+    return arr
+
+
+def _call(lib, arr, n, *, ns=5, coeffs=((3.4445, -4.775, 2.0315),), eps=1e-7, lr=0.02, mu=0.95,
+          wd=0.0, mode=0, ws=1 << 40, ws_bytes=1 << 60):
+    carr = (muon.MuonCoeff * max(1, len(coeffs)))(*[muon.MuonCoeff(*c) for c in coeffs])
+    return lib.muon_step(arr, n, lr, mu, wd, ns, carr if coeffs else None, len(coeffs), mode, eps,
+                         ctypes.c_void_p(ws), ws_bytes, None)
+
+
+GOOD = dict(param=0x10000000, grad=0x20000000, momentum=0x30000000, rows=64, cols=64,
+            grad_dtype=muon.MUON_BF16)
+
+
+def test_argument_errors_are_caught_on_the_host(lib):
+    ok = _mats([GOOD])
+    assert _call(lib, ok, 1, ns=-1) == muon.MUON_EINVAL
+    assert _call(lib, ok, 1, ns=65) == muon.MUON_EINVAL
+    assert _call(lib, ok, 1, coeffs=((1, 2, 3), (1, 2, 3))) == muon.MUON_EINVAL
+    assert _call(lib, ok, 1, eps=-1.0) == muon.MUON_EINVAL
+    assert _call(lib, ok, 1, lr=float("nan")) == muon.MUON_EINVAL
+    assert _call(lib, ok, 1, mode=7) == muon.MUON_EINVAL
+    assert _call(lib, ok, 1, coeffs=((float("inf"), 0, 0),)) == muon.MUON_EINVAL
+    assert _call(lib, ok, -1) == muon.MUON_EINVAL
+    assert _call(lib, _mats([dict(GOOD, rows=0)]), 1) == muon.MUON_EINVAL
+    assert _call(lib, _mats([dict(GOOD, param=0)]), 1) == muon.MUON_EINVAL
+    assert _call(lib, _mats([dict(GOOD, momentum=0)]), 1) == muon.MUON_EINVAL
+    assert _call(lib, _mats([dict(GOOD, grad_dtype=5)]), 1) == muon.MUON_EINVAL
+    assert _call(lib, _mats([dict(GOOD, param=0x10000002)]), 1) == muon.MUON_EINVAL
+
+
+def test_aliasing_is_rejected(lib):
+    # momentum overlapping the param, and two matrices sharing a param
+    assert _call(lib, _mats([dict(GOOD, momentum=GOOD["param"] + 64)]), 1) == muon.MUON_EALIAS
+    two = _mats([GOOD, dict(GOOD, grad=0x40000000, momentum=0x50000000)])
+    assert _call(lib, two, 2) == muon.MUON_EALIAS
+
+
+def test_workspace_errors(lib):
+    ok = _mats([GOOD])
+    need = lib.muon_workspace_bytes(ok, 1)
+    assert need > 0
+    assert _call(lib, ok, 1, ws=1 << 40, ws_bytes=need - 1) == muon.MUON_EWORKSPACE
+    assert _call(lib, ok, 1, ws=(1 << 40) + 16, ws_bytes=need) == muon.MUON_EWORKSPACE
+    assert _call(lib, ok, 1, ws=0, ws_bytes=need) == muon.MUON_EWORKSPACE
+
+
+def test_nothing_to_do_returns_ok_without_device(lib):
+    # all gradients absent: validated, then nothing is launched
+    skipped = _mats([dict(GOOD, grad=0)])
+    assert _call(lib, skipped, 1) == muon.MUON_OK
+    assert _call(lib, skipped, 0) == muon.MUON_OK
+
+
+def test_orthogonalize_argument_errors(lib):
+    arr = (muon.MuonOrtho * 1)()
+    arr[0].inp, arr[0].out, arr[0].rows, arr[0].cols, arr[0].in_dtype = 0x1000, 0x100000, 8, 8, 0
+    c = (muon.MuonCoeff * 1)(muon.MuonCoeff(3.4445, -4.775, 2.0315))
+    assert lib.muon_orthogonalize(arr, 1, 5, c, 2, 1e-7, ctypes.c_void_p(1 << 40), 1 << 40, None) == muon.MUON_EINVAL
+    arr[0].out = 0x1000 + 64
+    assert lib.muon_orthogonalize(arr, 1, 5, c, 1, 1e-7, ctypes.c_void_p(1 << 40), 1 << 40, None) == muon.MUON_EALIAS
+    arr[0].out = 0
+    assert lib.muon_orthogonalize(arr, 1, 5, c, 1, 1e-7, ctypes.c_void_p(1 << 40), 1 << 40, None) == muon.MUON_EINVAL
+
+
+def test_status_strings(lib):
+    for st in (muon.MUON_OK, muon.MUON_EINVAL, muon.MUON_EWORKSPACE, muon.MUON_EALIAS, muon.MUON_EHIP, -99):
+        assert isinstance(muon.status_string(st), str) and muon.status_string(st)
+    with pytest.raises(muon.LibMuonError):
+        _lib.check(muon.MUON_EINVAL, "x")
+
+
+def test_python_binding_validates_before_calling(lib):
+    torch = pytest.importorskip("torch")
+    p = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        muon.muon_step([p], [p], [p])                 # CPU tensors are refused
+    with pytest.raises(ValueError):
+        muon.muon_step([p], [p], [])
