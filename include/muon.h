@@ -23,8 +23,12 @@
  *        (airosetta.com newtonschulz5 loop; adg.csdn.net section
  *         "2. Newton-Schulz iteration"; the hybrid schedule of section
  *         "3. DeepSeek-V4 hybrid schedule" is a per-step coefficient list)
- *      X, A and B are held in bf16 (the pages cast to bf16); every product is
- *      accumulated in fp32 and rounded to bf16 once, to nearest-even.
+ *      X and A are held in bf16 (the pages cast to bf16); every product is
+ *      accumulated in fp32 and rounded to bf16 once, to nearest-even.  The
+ *      a_k X term is folded into the stored matrix, C = a_k I + b_k A +
+ *      c_k A A, so X <- C X; C is rounded to bf16 once, and for matrices
+ *      whose short side is <= 128 it is kept as a bf16 pair (C_hi + C_lo,
+ *      two MFMA passes) to stay well inside the bf16 error budget.
  *   5. decayed, scaled update:    p <- p*(1 - lr*wd) - lr*s*O
  *        (wmrh.cn section 4.2; adg.csdn.net section "3. Scaling and update")
  *      s = 1, or sqrt(max(1, rows/cols)) under MUON_SCALE_SQRT_MAX1 (the
@@ -151,15 +155,19 @@ int muon_orthogonalize(const muon_ortho_t* mats, int64_t n_mats, int ns_steps,
 /* Where matrix `index`'s intermediates live in the workspace after a call
  * over the same shapes (byte offsets from the workspace base).  Each bf16
  * buffer is zero-padded: X buffers are rows_pad x cols_pad in the stored
- * (rows x cols) orientation, A and B are m_pad x m_pad with m the short side.
+ * (rows x cols) orientation, A and C are m_pad x m_pad with m the short side.
  *   x_off[0]  X0 and every even iterate; x_off[1] the odd iterates.
+ *   a_off     A = X X^T of the last iteration.
+ *   c_off     C = a I + b A + c A A of the last iteration (bf16 high part).
+ *   c_lo_off  its low part C - bf16(C) (short side <= 128), else 0.
  *   o_off     the final iterate O for `ns_steps` iterations.
  *   nrm2_off  one double: sum of squares of M (of `in` for orthogonalize).
  * Host-only; launches nothing.  For tests and diagnostics. */
 typedef struct {
   size_t  x_off[2];
   size_t  a_off;
-  size_t  b_off;
+  size_t  c_off;
+  size_t  c_lo_off;
   size_t  o_off;
   size_t  nrm2_off;
   int64_t rows_pad;

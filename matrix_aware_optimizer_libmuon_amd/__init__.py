@@ -101,7 +101,8 @@ def workspace_view(shapes: Sequence, index: int, ns_steps: int) -> dict:
     _lib.check(_lib.load().muon_workspace_view(_shapes_array(shapes), len(shapes), int(index),
                                                int(ns_steps), ctypes.byref(v)),
                "muon_workspace_view")
-    return {"x_off": (v.x_off[0], v.x_off[1]), "a_off": v.a_off, "b_off": v.b_off,
+    return {"x_off": (v.x_off[0], v.x_off[1]), "a_off": v.a_off, "c_off": v.c_off,
+            "c_lo_off": v.c_lo_off,
             "o_off": v.o_off, "nrm2_off": v.nrm2_off, "rows_pad": v.rows_pad,
             "cols_pad": v.cols_pad, "m_pad": v.m_pad, "transposed": bool(v.transposed),
             "tile": v.tile}

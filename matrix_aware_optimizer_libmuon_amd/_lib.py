@@ -49,7 +49,7 @@ class MuonCoeff(ctypes.Structure):
 
 class MuonWorkspaceView(ctypes.Structure):
     _fields_ = [("x_off", ctypes.c_size_t * 2), ("a_off", ctypes.c_size_t),
-                ("b_off", ctypes.c_size_t), ("o_off", ctypes.c_size_t),
+                ("c_off", ctypes.c_size_t), ("c_lo_off", ctypes.c_size_t), ("o_off", ctypes.c_size_t),
                 ("nrm2_off", ctypes.c_size_t), ("rows_pad", ctypes.c_int64),
                 ("cols_pad", ctypes.c_int64), ("m_pad", ctypes.c_int64),
                 ("transposed", ctypes.c_int32), ("tile", ctypes.c_int32)]

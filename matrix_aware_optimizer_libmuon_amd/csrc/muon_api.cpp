@@ -31,12 +31,13 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 //
 //   [ table: MatDesc[n] | 4 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
 //   then, per matrix (all n, skipped ones included):
-//   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | B ] m_pad x m_pad bf16 each
+//   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | C ] m_pad x m_pad bf16 each,
+//   and [ C_lo ] m_pad x m_pad bf16 when the short side is <= kSplitMaxM
 // ---------------------------------------------------------------------------
 struct MatPlan {
   int64_t rows, cols, rows_pad, cols_pad, m_pad, n_pad;
-  bool tall;
-  size_t x_off[2], a_off, b_off;
+  bool tall, split;
+  size_t x_off[2], a_off, b_off, blo_off;
 };
 
 struct Plan {
@@ -75,6 +76,7 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
     m.tall = r > c;
     m.m_pad = m.tall ? m.cols_pad : m.rows_pad;
     m.n_pad = m.tall ? m.rows_pad : m.cols_pad;
+    m.split = std::min(r, c) <= kSplitMaxM;
     const size_t xb = static_cast<size_t>(m.rows_pad) * static_cast<size_t>(m.cols_pad) * 2;
     const size_t ab = static_cast<size_t>(m.m_pad) * static_cast<size_t>(m.m_pad) * 2;
     m.x_off[0] = off;
@@ -85,6 +87,11 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
     off = align_up(off + ab, kAlign);
     m.b_off = off;
     off = align_up(off + ab, kAlign);
+    m.blo_off = 0;
+    if (m.split) {
+      m.blo_off = off;
+      off = align_up(off + ab, kAlign);
+    }
   }
   plan.total = off;
   return true;
@@ -248,6 +255,7 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
     d.x[1] = reinterpret_cast<uint16_t*>(ws + m.x_off[1]);
     d.a = reinterpret_cast<uint16_t*>(ws + m.a_off);
     d.b = reinterpret_cast<uint16_t*>(ws + m.b_off);
+    d.blo = m.split ? reinterpret_cast<uint16_t*>(ws + m.blo_off) : nullptr;
     d.nrm2 = reinterpret_cast<double*>(ws + plan.nrm2_off) + i;
     d.rows = m.rows;
     d.cols = m.cols;
@@ -256,6 +264,7 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
     d.m_pad = static_cast<int32_t>(m.m_pad);
     d.n_pad = static_cast<int32_t>(m.n_pad);
     if (m.tall) d.flags |= kFlagTall;
+    if (m.split) d.flags |= kFlagSplitC;
     desc[a] = d;
     const int64_t flat = m.rows * m.cols;
     const int64_t padded = m.rows_pad * m.cols_pad;
@@ -296,9 +305,9 @@ int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float l
     const int parity = k & 1;
     rc = timed(kPhaseGram, stream, [&] { return launch_gram(d, pre[2], n, t.units[2], parity, s); });
     if (rc) return rc;
-    rc = timed(kPhaseGram2, stream, [&] { return launch_gram2(d, pre[2], n, t.units[2], c.b, c.c, s); });
+    rc = timed(kPhaseGram2, stream, [&] { return launch_gram2(d, pre[2], n, t.units[2], c.a, c.b, c.c, s); });
     if (rc) return rc;
-    rc = timed(kPhaseXUpdate, stream, [&] { return launch_xupdate(d, pre[3], n, t.units[3], parity, c.a, s); });
+    rc = timed(kPhaseXUpdate, stream, [&] { return launch_xupdate(d, pre[3], n, t.units[3], parity, s); });
     if (rc) return rc;
   }
   rc = timed(kPhaseApply, stream, [&] {
@@ -428,7 +437,8 @@ int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index
   view->x_off[0] = m.x_off[0];
   view->x_off[1] = m.x_off[1];
   view->a_off = m.a_off;
-  view->b_off = m.b_off;
+  view->c_off = m.b_off;
+  view->c_lo_off = m.split ? m.blo_off : 0;
   view->o_off = m.x_off[ns_steps & 1];
   view->nrm2_off = plan.nrm2_off + static_cast<size_t>(index) * sizeof(double);
   view->rows_pad = m.rows_pad;

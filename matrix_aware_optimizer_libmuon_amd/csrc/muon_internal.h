@@ -38,7 +38,14 @@ enum : uint32_t {
   kFlagGradBf16 = 2u,    // grad / input is bf16 (else fp32)
   kFlagVecFlat = 4u,     // param/grad/mom 16-byte aligned and rows*cols % 8 == 0
   kFlagVecRows = 8u,     // additionally cols % 8 == 0 (row-wise 8-vectors)
+  kFlagSplitC = 16u,     // C kept as a bf16 hi + lo pair (short side <= kSplitMaxM)
 };
+
+// Matrices whose short side is at most this keep C = a I + b A + c A A as a
+// pair of bf16 matrices (hi + lo) and run the X update as two MFMA passes.
+// Their Frobenius error then stays well inside the bf16 budget; the extra
+// pass is one 128-wide tile row, i.e. negligible work.
+constexpr int kSplitMaxM = 128;
 
 // One matrix, as the kernels see it.  128 bytes.
 struct alignas(16) MatDesc {
@@ -48,13 +55,14 @@ struct alignas(16) MatDesc {
   uint16_t* out;         // orthogonalize: bf16 rows x cols output / unused
   uint16_t* x[2];        // ping-pong bf16 X buffers, rows_pad x cols_pad
   uint16_t* a;           // bf16 m_pad x m_pad Gram
-  uint16_t* b;           // bf16 m_pad x m_pad b A + c A A
+  uint16_t* b;           // bf16 m_pad x m_pad C = a I + b A + c A A (high part)
+  uint16_t* blo;         // bf16 low part C - bf16(C) when kFlagSplitC, else null
   double* nrm2;          // sum of squares of M
   int64_t rows, cols;
   int32_t rows_pad, cols_pad, m_pad, n_pad;
   uint32_t flags;
   float scale;           // update scale s
-  int32_t reserved[4];
+  int32_t reserved[2];
 };
 static_assert(sizeof(MatDesc) == 128, "descriptor size");
 
@@ -65,10 +73,10 @@ int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t uni
                      float eps, void* stream);
 int launch_gram(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
                 void* stream);
-int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float b,
-                 float c, void* stream);
+int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a,
+                 float b, float c, void* stream);
 int launch_xupdate(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                   float a, void* stream);
+                   void* stream);
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
                  float lr, float wd, int export_only, void* stream);
 

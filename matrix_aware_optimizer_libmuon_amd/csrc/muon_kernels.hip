@@ -3,8 +3,8 @@
 //   K1 momentum + Frobenius sum of squares   (HBM-bound, one fp64 atomic per workgroup)
 //   K2 normalise + cast to bf16              (HBM-bound, writes the zero-padded X0)
 //   K3a Gram      A = X X^T                  (bf16 MFMA, upper-triangle tiles, mirrored store)
-//   K3b Gram^2    B = b A + c A A            (bf16 MFMA, A symmetric so A A = A A^T)
-//   K4  X update  X' = a X + B X             (bf16 MFMA, aX fused in the epilogue)
+//   K3b Gram^2    C = a I + b A + c A A      (bf16 MFMA, A symmetric so A A = A A^T)
+//   K4  X update  X' = C X                   (bf16 MFMA; a X folded into C)
 //   K5 apply      p <- p (1 - lr wd) - lr s O (HBM-bound)
 //
 // Every kernel is one grouped launch over all matrices of a call: workgroup
@@ -342,16 +342,19 @@ __device__ __forceinline__ void mma_step(const uint16_t* sp, const uint16_t* sq,
   }
 }
 
-// C_tile = P[mp0 : mp0+128, :K] * Q[nq0 : nq0+128, :K]^T   (K a multiple of 64)
-template <bool PMN, bool QMN>
-__device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t mp0, int64_t nq0,
-                                          int64_t K, uint16_t* smem, f32x16_t (&acc)[2][2]) {
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+}
+
+// acc += P[mp0 : mp0+128, :K] * Q[nq0 : nq0+128, :K]^T   (K a multiple of 64)
+template <bool PMN, bool QMN>
+__device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t mp0, int64_t nq0,
+                                          int64_t K, uint16_t* smem, f32x16_t (&acc)[2][2]) {
   // buffer k holds P at smem + 2k * kLdsTile and Q right after it
   u32x4 rp[4], rq[4];
   gload<PMN>(P, mp0, 0, rp);
@@ -384,15 +387,16 @@ __device__ __forceinline__ void acc_pos(int bi, int bj, int r, int& row, int& co
   col = 64 * (w & 1) + 32 * bj + (lane & 31);
 }
 
-enum Epi { kEpiGram = 0, kEpiGram2 = 1, kEpiXUpd = 2 };
-
 // Symmetric store of a Gram-type tile (ti <= tj): the tile and its mirror.
 // On a diagonal tile only the upper half (row <= col) is used for both
 // positions, so the stored matrix is exactly symmetric.
-template <int EPI>
+//   GRAM2 == false:  out = bf16(acc)                          (A = X X^T)
+//   GRAM2 == true:   C = a [row == col] + b A + c acc  (acc = A A), out = bf16(C),
+//                    and out_lo = bf16(C - out) when out_lo is given.
+template <bool GRAM2>
 __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t* out,
-                                          const uint16_t* src, int64_t ld, int64_t ti, int64_t tj,
-                                          float b, float c) {
+                                          uint16_t* out_lo, const uint16_t* src, int64_t ld,
+                                          int64_t ti, int64_t tj, float a, float b, float c) {
   const bool diag = ti == tj;
   const int64_t r0 = ti * BM, c0 = tj * BN;
 #pragma unroll
@@ -401,15 +405,18 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t*
     for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint16_t h[4];
+        uint16_t h[4], l[4];
         int row = 0, col = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc_pos(bi, bj, 4 * g + q, row, col);
           float v = acc[bi][bj][4 * g + q];
-          if constexpr (EPI == kEpiGram2)
-            v = fmaf(c, v, b * bf2f(gld<uint16_t>(src + (r0 + row) * ld + c0 + col)));
+          if constexpr (GRAM2) {
+            const float diag_a = (diag && row == col) ? a : 0.f;
+            v = fmaf(c, v, fmaf(b, bf2f(gld<uint16_t>(src + (r0 + row) * ld + c0 + col)), diag_a));
+          }
           h[q] = f2bf(v);
+          l[q] = f2bf(v - bf2f(h[q]));
         }
         acc_pos(bi, bj, 4 * g, row, col);  // rows row..row+3, one column
         if (!diag) {
@@ -419,12 +426,23 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t*
           m.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
           m.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
           gst<u32x2>(out + (c0 + col) * ld + r0 + row, m);
+          if (GRAM2 && out_lo) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gst<uint16_t>(out_lo + (r0 + row + q) * ld + c0 + col, l[q]);
+            m.x = l[0] | (static_cast<uint32_t>(l[1]) << 16);
+            m.y = l[2] | (static_cast<uint32_t>(l[3]) << 16);
+            gst<u32x2>(out_lo + (c0 + col) * ld + r0 + row, m);
+          }
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             if (row + q <= col) {
               gst<uint16_t>(out + (r0 + row + q) * ld + c0 + col, h[q]);
               gst<uint16_t>(out + (c0 + col) * ld + r0 + row + q, h[q]);
+              if (GRAM2 && out_lo) {
+                gst<uint16_t>(out_lo + (r0 + row + q) * ld + c0 + col, l[q]);
+                gst<uint16_t>(out_lo + (c0 + col) * ld + r0 + row + q, l[q]);
+              }
             }
           }
         }
@@ -463,17 +481,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gram(const MatDesc* __restrict
   decode_sym(unit - prefix[i], d.m_pad / BM, ti, tj);
   const Opnd X{d.x[parity], d.cols_pad};
   f32x16_t acc[2][2];
+  zero_acc(acc);
   if (d.flags & kFlagTall)
     gemm_tile<true, true>(X, X, ti * BM, tj * BN, d.rows_pad, smem, acc);
   else
     gemm_tile<false, false>(X, X, ti * BM, tj * BN, d.cols_pad, smem, acc);
-  store_sym<kEpiGram>(acc, d.a, nullptr, d.m_pad, ti, tj, 0.f, 0.f);
+  store_sym<false>(acc, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f);
 }
 
-// K3b: B = b A + c A A  (A symmetric: A A = A A^T, a K-contiguous "NT" product)
+// K3b: C = a I + b A + c A A  (A symmetric: A A = A A^T, a K-contiguous product).
+// Folding a X into C (X' = C X) keeps the large cancelling terms of the
+// polynomial inside one fp32 sum before the single bf16 rounding.
 __global__ __launch_bounds__(kGemmThreads) void k_gram2(const MatDesc* __restrict__ descs,
                                                         const int64_t* __restrict__ prefix, int n,
-                                                        int64_t units, float b, float c) {
+                                                        int64_t units, float a, float b, float c) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kLdsTile];
   const int64_t unit = xcd_remap(blockIdx.x, units);
   const int i = find_matrix(prefix, n, unit);
@@ -482,16 +503,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gram2(const MatDesc* __restric
   decode_sym(unit - prefix[i], d.m_pad / BM, ti, tj);
   const Opnd A{d.a, d.m_pad};
   f32x16_t acc[2][2];
+  zero_acc(acc);
   gemm_tile<false, false>(A, A, ti * BM, tj * BN, d.m_pad, smem, acc);
-  store_sym<kEpiGram2>(acc, d.b, d.a, d.m_pad, ti, tj, b, c);
+  store_sym<true>(acc, d.b, (d.flags & kFlagSplitC) ? d.blo : nullptr, d.a, d.m_pad, ti, tj, a, b, c);
 }
 
-// K4: X' = a X + B X.  Wide (rows <= cols): X'[i][k] = a X[i][k] + sum_j B[i][j] X[j][k].
-// Tall: the stored matrix is X^T, so X'^T = a X^T + X^T B (B symmetric).
+// K4: X' = C X.  Wide (rows <= cols): X'[i][k] = sum_j C[i][j] X[j][k].
+// Tall: the stored matrix is X^T, so X'^T = X^T C (C symmetric).
+// Split matrices add the low part: X' = C_hi X + C_lo X.
 __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restrict__ descs,
                                                           const int64_t* __restrict__ prefix,
-                                                          int n, int64_t units, int parity,
-                                                          float a) {
+                                                          int n, int64_t units, int parity) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kLdsTile];
   const int64_t unit = xcd_remap(blockIdx.x, units);
   const int i = find_matrix(prefix, n, unit);
@@ -501,11 +523,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
   const uint16_t* x = d.x[parity];
   uint16_t* xn = d.x[parity ^ 1];
   const int64_t ld = d.cols_pad;
+  const bool split = (d.flags & kFlagSplitC) != 0;
   f32x16_t acc[2][2];
-  if (d.flags & kFlagTall)
+  zero_acc(acc);
+  if (d.flags & kFlagTall) {
     gemm_tile<false, false>(Opnd{x, ld}, Opnd{d.b, d.m_pad}, ti * BM, tj * BN, d.m_pad, smem, acc);
-  else
+    if (split)
+      gemm_tile<false, false>(Opnd{x, ld}, Opnd{d.blo, d.m_pad}, ti * BM, tj * BN, d.m_pad, smem, acc);
+  } else {
     gemm_tile<false, true>(Opnd{d.b, d.m_pad}, Opnd{x, ld}, ti * BM, tj * BN, d.m_pad, smem, acc);
+    if (split)
+      gemm_tile<false, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * BM, tj * BN, d.m_pad, smem, acc);
+  }
   const int64_t r0 = ti * BM, c0 = tj * BN;
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
@@ -515,8 +544,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
       for (int r = 0; r < 16; ++r) {
         int row, col;
         acc_pos(bi, bj, r, row, col);
-        const int64_t off = (r0 + row) * ld + c0 + col;
-        gst<uint16_t>(xn + off, f2bf(fmaf(a, bf2f(gld<uint16_t>(x + off)), acc[bi][bj][r])));
+        gst<uint16_t>(xn + (r0 + row) * ld + c0 + col, f2bf(acc[bi][bj][r]));
       }
 }
 
@@ -549,19 +577,19 @@ int launch_gram(const MatDesc* d, const int64_t* prefix, int n, int64_t units, i
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float b, float c,
-                 void* stream) {
+int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a, float b,
+                 float c, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_gram2, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, units, b, c);
+                     static_cast<hipStream_t>(stream), d, prefix, n, units, a, b, c);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_xupdate(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                   float a, void* stream) {
+                   void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_xupdate, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, units, parity, a);
+                     static_cast<hipStream_t>(stream), d, prefix, n, units, parity);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -80,9 +80,17 @@ class Run:
         v = self.view(i)
         return bf16_to_np(self.ws_bf16(v["a_off"], v["m_pad"], v["m_pad"]))
 
-    def b(self, i):
+    def c(self, i):
+        """C = a I + b A + c A A (bf16 high part) of the last iteration."""
         v = self.view(i)
-        return bf16_to_np(self.ws_bf16(v["b_off"], v["m_pad"], v["m_pad"]))
+        return bf16_to_np(self.ws_bf16(v["c_off"], v["m_pad"], v["m_pad"]))
+
+    def c_lo(self, i):
+        """Low part of C (short side <= 128), else None."""
+        v = self.view(i)
+        if v["c_lo_off"] == 0:
+            return None
+        return bf16_to_np(self.ws_bf16(v["c_lo_off"], v["m_pad"], v["m_pad"]))
 
     def nu(self, i):
         off = self.view(i)["nrm2_off"]

@@ -113,12 +113,14 @@ def test_grouped_dispatch_equals_one_by_one_and_is_order_free():
         assert np.array_equal(grouped.param(i), alone[i].param(0)) or rel(grouped.param(i), alone[i].param(0)) <= 1e-7
 
 
-@pytest.mark.parametrize("shape", [(200, 300), (300, 200), (256, 256), (40, 600)])
+@pytest.mark.parametrize("shape", [(200, 300), (300, 200), (256, 256), (40, 600), (600, 100)])
 def test_stage_consistency_of_the_gemm_kernels(shape):
     """One iteration (ns = 1) read stage by stage from the workspace: every
-    bf16 result is the round-to-nearest of the exact product of the
-    library's own bf16 operands, up to fp32 accumulation error.  A and B are
-    exactly symmetric, padding stays zero."""
+    bf16 result is the round-to-nearest of the exact value computed from the
+    library's own bf16 operands, up to fp32 accumulation error:
+        A = X0 X0^T,  C = a I + b A + c A A (+ its low part when the short
+        side is <= 128),  X1 = C X0 (= (C_hi + C_lo) X0).
+    A and C are exactly symmetric; padding stays zero."""
     r, c = shape
     a_, b_, c_ = muon.QUINTIC
     mi = W.adhoc_inputs(r, c, "bf16", seed=21)
@@ -128,27 +130,39 @@ def test_stage_consistency_of_the_gemm_kernels(shape):
     x0 = run.x(0, 0).astype(np.float64)
     x1 = run.x(0, 1).astype(np.float64)
     A = run.a(0).astype(np.float64)
-    B = run.b(0).astype(np.float64)
-    assert np.array_equal(A, A.T) and np.array_equal(B, B.T)
+    C = run.c(0).astype(np.float64)
+    C_lo = run.c_lo(0)
+    assert (C_lo is not None) == (m <= 128)
+    assert np.array_equal(A, A.T) and np.array_equal(C, C.T)
     tall = r > c
     X = x0.T if tall else x0            # logical m x n view (padded)
     Xn = x1.T if tall else x1
-    u = 2.0 ** -8                       # bf16 rounding (RNE: <= 2^-9) with slack
+    u = 2.0 ** -8                       # bf16 unit roundoff (round to nearest)
+    g = 2.0 ** -22                      # 4x the fp32 unit roundoff, per accumulated term
     K = X.shape[1]
     exact_A = X @ X.T
-    bound_A = u * np.abs(exact_A) + 2.0 ** -22 * K * (np.abs(X) @ np.abs(X).T) + 1e-30
-    assert np.all(np.abs(A - exact_A) <= bound_A), "Gram"
-    AA = A @ A
-    exact_B = b_ * A + c_ * AA
-    bound_B = u * np.abs(exact_B) + 2.0 ** -22 * (A.shape[0] * abs(c_) * (np.abs(A) @ np.abs(A)) + np.abs(b_ * A))
-    assert np.all(np.abs(B - exact_B) <= bound_B + 1e-30), "Gram^2 epilogue"
-    exact_X = a_ * X + B @ X
-    bound_X = u * np.abs(exact_X) + 2.0 ** -22 * (B.shape[0] * (np.abs(B) @ np.abs(X)) + np.abs(a_ * X))
+    bound_A = u * np.abs(exact_A) + g * K * (np.abs(X) @ np.abs(X).T)
+    assert np.all(np.abs(A - exact_A) <= bound_A + 1e-30), "Gram"
+    # a sits on the whole padded diagonal; harmless, since X's padding is zero
+    exact_C = a_ * np.eye(A.shape[0]) + b_ * A + c_ * (A @ A)
+    acc_C = g * (A.shape[0] * abs(c_) * (np.abs(A) @ np.abs(A)) + np.abs(b_ * A) + abs(a_))
+    if C_lo is None:
+        assert np.all(np.abs(C - exact_C) <= u * np.abs(exact_C) + acc_C + 1e-30), "C epilogue"
+        Cfull = C
+    else:
+        C_lo = C_lo.astype(np.float64)
+        assert np.array_equal(C_lo, C_lo.T)
+        Cfull = C + C_lo                  # hi + lo carries ~16 significant bits
+        assert np.all(np.abs(Cfull - exact_C) <= 2.0 ** -16 * np.abs(exact_C) + acc_C + 1e-30), "C pair"
+        assert np.all(np.abs(C_lo) <= 2.0 ** -8 * np.abs(C) + 1e-30)
+    exact_X = Cfull @ X
+    bound_X = u * np.abs(exact_X) + g * 2 * Cfull.shape[0] * (np.abs(Cfull) @ np.abs(X))
     assert np.all(np.abs(Xn - exact_X) <= bound_X + 1e-30), "X update"
     # zero padding outside the m x n block is preserved by every stage
-    assert np.all(A[m:, :] == 0) and np.all(B[:, m:] == 0)
+    assert np.all(A[m:, :] == 0) and np.all(A[:, m:] == 0)
     assert np.all(x1[r:, :] == 0) and np.all(x1[:, c:] == 0) and np.all(x0[r:, :] == 0)
-    say(f"  {shape}: pads {v['rows_pad']}x{v['cols_pad']} m_pad {v['m_pad']} ok")
+    assert np.all(x0[:, c:] == 0)
+    say(f"  {shape}: pads {v['rows_pad']}x{v['cols_pad']} m_pad {v['m_pad']} split {C_lo is not None} ok")
 
 
 def test_orthogonalize_ns0_is_round_to_nearest_of_normalised_input():

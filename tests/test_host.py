@@ -45,7 +45,7 @@ def test_struct_layouts_match_header(lib):
     assert ctypes.sizeof(muon.MuonMatrix) == 48
     assert ctypes.sizeof(muon.MuonOrtho) == 40
     assert ctypes.sizeof(muon.MuonCoeff) == 12
-    assert ctypes.sizeof(muon.MuonWorkspaceView) == 80
+    assert ctypes.sizeof(muon.MuonWorkspaceView) == 88
 
 
 def test_workspace_plan(lib):
@@ -62,9 +62,14 @@ def test_workspace_plan(lib):
         ab = v["m_pad"] ** 2 * 2
         assert v["x_off"][0] % 256 == 0 and v["x_off"][0] >= end
         assert v["x_off"][1] >= v["x_off"][0] + xb
-        assert v["a_off"] >= v["x_off"][1] + xb and v["b_off"] >= v["a_off"] + ab
+        assert v["a_off"] >= v["x_off"][1] + xb and v["c_off"] >= v["a_off"] + ab
         assert v["o_off"] == v["x_off"][1]          # 5 iterations end in the odd buffer
-        end = v["b_off"] + ab
+        end = v["c_off"] + ab
+        if min(r, c) <= 128:                         # short side <= 128: low part of C kept
+            assert v["c_lo_off"] >= end
+            end = v["c_lo_off"] + ab
+        else:
+            assert v["c_lo_off"] == 0
     assert end <= total
     assert muon.workspace_view(shapes, 0, 4)["o_off"] == views[0]["x_off"][0]
     nrm = [v["nrm2_off"] for v in views]
