@@ -29,20 +29,28 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 // workspace plan (a pure function of the shapes)
 //
-//   [ table: MatDesc[n] | 4 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
+//   [ table: MatDesc[n] | 6 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
 //   then, per matrix (all n, skipped ones included):
 //   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | C ] m_pad x m_pad bf16 each,
 //   and [ C_lo ] m_pad x m_pad bf16 when the short side is <= kSplitMaxM
 // ---------------------------------------------------------------------------
+// prefix arrays of the table: element chunks (flat / padded) over all active
+// matrices, then symmetric and full tile counts per tile class
+enum { kPreFlat = 0, kPrePad = 1, kPreSymBig = 2, kPreFullBig = 3, kPreSymSmall = 4,
+       kPreFullSmall = 5, kNumPrefix = 6 };
+
+int tile_class(int64_t r, int64_t c) { return std::min(r, c) >= kBigMinM ? kTileBig : kTileSmall; }
+
 struct MatPlan {
   int64_t rows, cols, rows_pad, cols_pad, m_pad, n_pad;
+  int tile;
   bool tall, split;
   size_t x_off[2], a_off, b_off, blo_off;
 };
 
 struct Plan {
   int64_t n = 0;
-  size_t desc_off = 0, prefix_off[4] = {0, 0, 0, 0}, nrm2_off = 0, table_bytes = 0;
+  size_t desc_off = 0, prefix_off[kNumPrefix] = {0, 0, 0, 0, 0, 0}, nrm2_off = 0, table_bytes = 0;
   size_t total = 0;
   std::vector<MatPlan> mats;
 };
@@ -55,7 +63,7 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
   plan.n = n;
   plan.desc_off = 0;
   size_t off = static_cast<size_t>(n) * sizeof(MatDesc);
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kNumPrefix; ++k) {
     plan.prefix_off[k] = off;
     off += static_cast<size_t>(n + 1) * sizeof(int64_t);
   }
@@ -71,8 +79,9 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
     MatPlan& m = plan.mats[static_cast<size_t>(i)];
     m.rows = r;
     m.cols = c;
-    m.rows_pad = round_up(r, kTile);
-    m.cols_pad = round_up(c, kTile);
+    m.tile = tile_class(r, c);
+    m.rows_pad = round_up(r, m.tile);
+    m.cols_pad = round_up(c, m.tile);
     m.tall = r > c;
     m.m_pad = m.tall ? m.cols_pad : m.rows_pad;
     m.n_pad = m.tall ? m.rows_pad : m.cols_pad;
@@ -209,7 +218,8 @@ int timed(int phase, hipStream_t stream, F&& launch) {
 struct Table {
   std::vector<unsigned char> bytes;
   int n_active = 0;
-  int64_t units[4] = {0, 0, 0, 0};  // flat chunks, padded chunks, sym tiles, full tiles
+  int n_big = 0;                      // descriptors [0, n_big) are 256-tile matrices
+  int64_t units[kNumPrefix] = {0, 0, 0, 0, 0, 0};
 };
 
 bool finite(float x) { return std::isfinite(x); }
@@ -235,52 +245,66 @@ bool any_overlap(std::vector<std::pair<uintptr_t, uintptr_t>>& r) {
   return false;
 }
 
-// Fill the descriptor table for the active matrices.
+// Fill the descriptor table for the active matrices: 256-tile matrices first,
+// then 128-tile ones, so each GEMM class is one contiguous descriptor range.
 template <class Fill>
 void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) {
   const size_t n = static_cast<size_t>(plan.n);
   t.bytes.assign(plan.table_bytes, 0);
   t.n_active = n_active;
   MatDesc* desc = reinterpret_cast<MatDesc*>(t.bytes.data() + plan.desc_off);
-  int64_t* pre[4];
-  for (int k = 0; k < 4; ++k) pre[k] = reinterpret_cast<int64_t*>(t.bytes.data() + plan.prefix_off[k]);
-  int64_t acc[4] = {0, 0, 0, 0};
+  int64_t* pre[kNumPrefix];
+  for (int k = 0; k < kNumPrefix; ++k)
+    pre[k] = reinterpret_cast<int64_t*>(t.bytes.data() + plan.prefix_off[k]);
+  int64_t acc[kNumPrefix] = {0, 0, 0, 0, 0, 0};
   int a = 0;
-  for (size_t i = 0; i < n; ++i) {
-    const MatPlan& m = plan.mats[i];
-    MatDesc d;
-    std::memset(&d, 0, sizeof(d));
-    if (!fill(i, d)) continue;
-    d.x[0] = reinterpret_cast<uint16_t*>(ws + m.x_off[0]);
-    d.x[1] = reinterpret_cast<uint16_t*>(ws + m.x_off[1]);
-    d.a = reinterpret_cast<uint16_t*>(ws + m.a_off);
-    d.b = reinterpret_cast<uint16_t*>(ws + m.b_off);
-    d.blo = m.split ? reinterpret_cast<uint16_t*>(ws + m.blo_off) : nullptr;
-    d.nrm2 = reinterpret_cast<double*>(ws + plan.nrm2_off) + i;
-    d.rows = m.rows;
-    d.cols = m.cols;
-    d.rows_pad = static_cast<int32_t>(m.rows_pad);
-    d.cols_pad = static_cast<int32_t>(m.cols_pad);
-    d.m_pad = static_cast<int32_t>(m.m_pad);
-    d.n_pad = static_cast<int32_t>(m.n_pad);
-    if (m.tall) d.flags |= kFlagTall;
-    if (m.split) d.flags |= kFlagSplitC;
-    desc[a] = d;
-    const int64_t flat = m.rows * m.cols;
-    const int64_t padded = m.rows_pad * m.cols_pad;
-    const int64_t t_side = m.m_pad / kTile;
-    const int64_t units[4] = {(flat + kChunk - 1) / kChunk, (padded + kChunk - 1) / kChunk,
-                              t_side * (t_side + 1) / 2, (m.rows_pad / kTile) * (m.cols_pad / kTile)};
-    for (int k = 0; k < 4; ++k) {
-      pre[k][a] = acc[k];
-      acc[k] += units[k];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int want = pass == 0 ? kTileBig : kTileSmall;
+    const int sym = pass == 0 ? kPreSymBig : kPreSymSmall;
+    const int full = pass == 0 ? kPreFullBig : kPreFullSmall;
+    int local = 0;
+    for (size_t i = 0; i < n; ++i) {
+      const MatPlan& m = plan.mats[i];
+      if (m.tile != want) continue;
+      MatDesc d;
+      std::memset(&d, 0, sizeof(d));
+      if (!fill(i, d)) continue;
+      d.x[0] = reinterpret_cast<uint16_t*>(ws + m.x_off[0]);
+      d.x[1] = reinterpret_cast<uint16_t*>(ws + m.x_off[1]);
+      d.a = reinterpret_cast<uint16_t*>(ws + m.a_off);
+      d.b = reinterpret_cast<uint16_t*>(ws + m.b_off);
+      d.blo = m.split ? reinterpret_cast<uint16_t*>(ws + m.blo_off) : nullptr;
+      d.nrm2 = reinterpret_cast<double*>(ws + plan.nrm2_off) + i;
+      d.rows = m.rows;
+      d.cols = m.cols;
+      d.rows_pad = static_cast<int32_t>(m.rows_pad);
+      d.cols_pad = static_cast<int32_t>(m.cols_pad);
+      d.m_pad = static_cast<int32_t>(m.m_pad);
+      d.n_pad = static_cast<int32_t>(m.n_pad);
+      if (m.tall) d.flags |= kFlagTall;
+      if (m.split) d.flags |= kFlagSplitC;
+      desc[a] = d;
+      const int64_t flat = m.rows * m.cols;
+      const int64_t padded = m.rows_pad * m.cols_pad;
+      const int64_t t_side = m.m_pad / m.tile;
+      pre[kPreFlat][a] = acc[kPreFlat];
+      acc[kPreFlat] += (flat + kChunk - 1) / kChunk;
+      pre[kPrePad][a] = acc[kPrePad];
+      acc[kPrePad] += (padded + kChunk - 1) / kChunk;
+      pre[sym][local] = acc[sym];
+      acc[sym] += t_side * (t_side + 1) / 2;
+      pre[full][local] = acc[full];
+      acc[full] += (m.rows_pad / m.tile) * (m.cols_pad / m.tile);
+      ++a;
+      ++local;
     }
-    ++a;
+    pre[sym][local] = acc[sym];
+    pre[full][local] = acc[full];
+    if (pass == 0) t.n_big = local;
   }
-  for (int k = 0; k < 4; ++k) {
-    pre[k][a] = acc[k];
-    t.units[k] = acc[k];
-  }
+  pre[kPreFlat][a] = acc[kPreFlat];
+  pre[kPrePad][a] = acc[kPrePad];
+  for (int k = 0; k < kNumPrefix; ++k) t.units[k] = acc[k];
 }
 
 int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float lr, float mu,
@@ -290,28 +314,46 @@ int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float l
   if (rc != MUON_OK) return rc;
   if (t.n_active == 0) return MUON_OK;
   const MatDesc* d = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
-  const int64_t* pre[4];
-  for (int k = 0; k < 4; ++k) pre[k] = reinterpret_cast<const int64_t*>(ws + plan.prefix_off[k]);
-  const int n = t.n_active;
+  const int64_t* pre[kNumPrefix];
+  for (int k = 0; k < kNumPrefix; ++k) pre[k] = reinterpret_cast<const int64_t*>(ws + plan.prefix_off[k]);
+  const int n = t.n_active, nb = t.n_big, ns = n - nb;
+  const MatDesc* d_small = d + nb;
   void* s = static_cast<void*>(stream);
   rc = timed(kPhaseMomentumNorm, stream, [&] {
-    return launch_momentum_norm(d, pre[0], n, t.units[0], mu, ortho ? 1 : 0, s);
+    return launch_momentum_norm(d, pre[kPreFlat], n, t.units[kPreFlat], mu, ortho ? 1 : 0, s);
   });
   if (rc) return rc;
-  rc = timed(kPhaseNormalize, stream, [&] { return launch_normalize(d, pre[1], n, t.units[1], eps, s); });
+  rc = timed(kPhaseNormalize, stream, [&] {
+    return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, s);
+  });
   if (rc) return rc;
   for (int k = 0; k < ns_steps; ++k) {
     const muon_ns_coeff_t& c = coeffs[n_coeffs == 1 ? 0 : k];
     const int parity = k & 1;
-    rc = timed(kPhaseGram, stream, [&] { return launch_gram(d, pre[2], n, t.units[2], parity, s); });
+    rc = timed(kPhaseGram, stream, [&] {
+      int e = 0;
+      if (nb) e = launch_gram(kTileBig, d, pre[kPreSymBig], nb, t.units[kPreSymBig], parity, s);
+      if (!e && ns) e = launch_gram(kTileSmall, d_small, pre[kPreSymSmall], ns, t.units[kPreSymSmall], parity, s);
+      return e;
+    });
     if (rc) return rc;
-    rc = timed(kPhaseGram2, stream, [&] { return launch_gram2(d, pre[2], n, t.units[2], c.a, c.b, c.c, s); });
+    rc = timed(kPhaseGram2, stream, [&] {
+      int e = 0;
+      if (nb) e = launch_gram2(kTileBig, d, pre[kPreSymBig], nb, t.units[kPreSymBig], c.a, c.b, c.c, s);
+      if (!e && ns) e = launch_gram2(kTileSmall, d_small, pre[kPreSymSmall], ns, t.units[kPreSymSmall], c.a, c.b, c.c, s);
+      return e;
+    });
     if (rc) return rc;
-    rc = timed(kPhaseXUpdate, stream, [&] { return launch_xupdate(d, pre[3], n, t.units[3], parity, s); });
+    rc = timed(kPhaseXUpdate, stream, [&] {
+      int e = 0;
+      if (nb) e = launch_xupdate(kTileBig, d, pre[kPreFullBig], nb, t.units[kPreFullBig], parity, s);
+      if (!e && ns) e = launch_xupdate(kTileSmall, d_small, pre[kPreFullSmall], ns, t.units[kPreFullSmall], parity, s);
+      return e;
+    });
     if (rc) return rc;
   }
   rc = timed(kPhaseApply, stream, [&] {
-    return launch_apply(d, pre[0], n, t.units[0], ns_steps & 1, lr, wd, ortho ? 1 : 0, s);
+    return launch_apply(d, pre[kPreFlat], n, t.units[kPreFlat], ns_steps & 1, lr, wd, ortho ? 1 : 0, s);
   });
   return rc;
 }
@@ -445,7 +487,7 @@ int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index
   view->cols_pad = m.cols_pad;
   view->m_pad = m.m_pad;
   view->transposed = m.tall ? 1 : 0;
-  view->tile = kTile;
+  view->tile = m.tile;
   return MUON_OK;
 }
 

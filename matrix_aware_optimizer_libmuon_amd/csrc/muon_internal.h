@@ -10,11 +10,15 @@
 
 namespace muon {
 
-// Output tile of the Newton-Schulz GEMMs and padding granule of every bf16
-// workspace buffer.  All X / A / B buffers are zero-padded to multiples of
-// kTile in both dimensions, so the GEMM kernels never need bounds checks:
-// zero rows and columns of X keep producing exact zeros in A, B and X'.
-constexpr int kTile = 128;
+// Output tile of the Newton-Schulz GEMMs and padding granule of a matrix's
+// bf16 workspace buffers.  Each matrix belongs to one tile class: 256 x 256
+// tiles when its short side is at least kBigMinM, else 128 x 128.  All X / A
+// / C buffers are zero-padded to multiples of the class tile in both
+// dimensions, so the GEMM kernels never need bounds checks: zero rows and
+// columns of X keep producing exact zeros in A and X'.
+constexpr int kTileSmall = 128;
+constexpr int kTileBig = 256;
+constexpr int kBigMinM = 1024;
 // Depth of one K step of the GEMM main loop.
 constexpr int kTileK = 64;
 // Elements handled by one workgroup of the elementwise phases.
@@ -71,12 +75,13 @@ int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t
                          float mu, int norm_only, void* stream);
 int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                      float eps, void* stream);
-int launch_gram(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                void* stream);
-int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a,
-                 float b, float c, void* stream);
-int launch_xupdate(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                   void* stream);
+// GEMM phases: `tile` is 128 or 256; every matrix of the launch is of that class
+int launch_gram(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                int parity, void* stream);
+int launch_gram2(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                 float a, float b, float c, void* stream);
+int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                   int parity, void* stream);
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
                  float lr, float wd, int export_only, void* stream);
 

@@ -242,27 +242,56 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
 }
 
 // ---------------------------------------------------------------------------
-// Newton-Schulz GEMMs on bf16 MFMA (v_mfma_f32_32x32x16_bf16)
+// Newton-Schulz GEMM engine on bf16 MFMA (v_mfma_f32_32x32x16_bf16)
 //
-// Workgroup tile 128 x 128, K step 64, 4 waves in a 2 x 2 grid, each wave
-// 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Operands are staged in LDS as
-// [row][k] with k contiguous; the 16-byte chunk c of row r is stored at
-// chunk c ^ swz(r), so that the 32 rows an MFMA fragment read touches spread
-// over all banks.  Two LDS buffers: the next K step's global loads are in
-// flight while the current one is multiplied; one barrier per K step.
+// Output tile TILE x TILE (128 or 256), K step 32, 4 waves in a 2 x 2 grid,
+// each wave (TILE/2) x (TILE/2) = NB x NB MFMA blocks of 32 x 32 with fp32
+// accumulators (256 of them per lane at TILE = 256, held in AGPRs).
+//
+// Operand tiles go straight from global memory into LDS (16 bytes per lane,
+// no register staging, no LDS store instructions): on this chip LDS stores
+// from registers run at about two thirds of the LDS read rate and were the
+// limit.  Four LDS stages; loads run three K steps ahead; one barrier per K
+// step, placed between its two 16-deep MFMA substeps so the fragments of
+// the next step are read while the second substep's MFMAs run.
 //
 // An operand is "K-contiguous" (element (mn, k) at p[mn * ld + k]) or
-// "MN-contiguous" (element (mn, k) at p[k * ld + mn]).  MN-contiguous tiles
-// are transposed in registers (4 k x 8 mn blocks) on their way into LDS, so
-// the inner loop is the same for every layout: the transpose of a tall
-// matrix is never materialised.
+// "MN-contiguous" (element (mn, k) at p[k * ld + mn]).
+//   K-contiguous tiles sit in LDS as [mn][32 k] (64-byte rows); fragments
+//     are 16-byte reads; the 16-byte chunk c of row r is stored at
+//     c ^ ((r >> 1) & 3), which spreads the 8 rows read per cycle over all
+//     banks.
+//   MN-contiguous tiles keep their memory layout, [k][TILE mn]; fragments
+//     are assembled by the LDS transpose read (ds_read_b64_tr_b16: in each
+//     16-lane group, lane 4a + b receives element b of the 8-byte blocks
+//     addressed by lanes a, a + 4, a + 8, a + 12), so the transpose of a tall
+//     matrix is never materialised, not even in registers.  The 16-byte
+//     chunk c of k row r is stored at c ^ (2 (r & 3)): the four k rows one
+//     transpose read touches then hit distinct banks.
 // ---------------------------------------------------------------------------
-constexpr int BM = kTile, BN = kTile, BK = kTileK;
-constexpr int kLdsTile = BM * BK;  // bf16 elements per staged operand tile
+constexpr int BK = 32;
+constexpr int kStages = 4;
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_idx(int row, int chunk) {
-  return row * BK + ((chunk ^ swz(row)) << 3);
+template <int TILE>
+struct Geo {
+  static constexpr int T = TILE;
+  static constexpr int WT = TILE / 2;      // wave tile
+  static constexpr int NB = WT / 32;       // 32x32 MFMA blocks per wave side
+  static constexpr int TE = TILE * BK;     // bf16 elements of one staged operand tile
+  static constexpr int LPW = TILE / 64;    // 1 KB direct loads per wave per operand tile
+  static constexpr int LDS = kStages * 2 * TE * 2;  // bytes
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N global -> LDS loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 struct Opnd {
@@ -270,121 +299,161 @@ struct Opnd {
   int64_t ld;
 };
 
-// global -> registers for one 128 x 64 operand tile
-template <bool MN>
-__device__ __forceinline__ void gload(const Opnd& op, int64_t mn0, int64_t k0, u32x4 (&r)[4]) {
-  const int t = threadIdx.x;
-  if constexpr (!MN) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = (t >> 3) + 32 * j, chunk = t & 7;
-      r[j] = gld<u32x4>(op.p + (mn0 + row) * op.ld + k0 + chunk * 8);
-    }
-  } else {
-    const int kq = t >> 4, mc = t & 15;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r[j] = gld<u32x4>(op.p + (k0 + 4 * kq + j) * op.ld + mn0 + 8 * mc);
-  }
+// Global -> LDS, 16 bytes per lane, without registers.  Written as a one-line
+// asm statement: it writes only LDS (no register results), and the compiler
+// would otherwise assume every later LDS read may alias these writes and wait
+// for all of them.  Ordering is explicit instead: vm_wait<> on the issuing
+// wave, then an LDS barrier, before any wave reads the stage.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_dst) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) void*)lds_dst));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0));
 }
 
-// registers -> LDS (transposing MN-contiguous tiles)
-template <bool MN>
-__device__ __forceinline__ void lstore(uint16_t* s, const u32x4 (&r)[4]) {
-  const int t = threadIdx.x;
-  if constexpr (!MN) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = (t >> 3) + 32 * j, chunk = t & 7;
-      *reinterpret_cast<u32x4*>(s + lds_idx(row, chunk)) = r[j];
-    }
-  } else {
-    const int kq = t >> 4, mc = t & 15;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // dword q of each k row holds mn = 2q (low half) and mn = 2q + 1 (high half)
-      u32x2 lo, hi;
-      lo.x = (r[0][q] & 0xffffu) | (r[1][q] << 16);
-      lo.y = (r[2][q] & 0xffffu) | (r[3][q] << 16);
-      hi.x = (r[0][q] >> 16) | (r[1][q] & 0xffff0000u);
-      hi.y = (r[2][q] >> 16) | (r[3][q] & 0xffff0000u);
-      const int row0 = 8 * mc + 2 * q;
-      *reinterpret_cast<u32x2*>(s + lds_idx(row0, kq >> 1) + (kq & 1) * 4) = lo;
-      *reinterpret_cast<u32x2*>(s + lds_idx(row0 + 1, kq >> 1) + (kq & 1) * 4) = hi;
-    }
-  }
-}
-
-// acc[bi][bj] += P(rows of this wave) * Q(cols of this wave)^T over one K step
-__device__ __forceinline__ void mma_step(const uint16_t* sp, const uint16_t* sq,
-                                         f32x16_t (&acc)[2][2]) {
+// Block q of this wave's share of a TILE x 32 operand tile.  The tile is
+// TILE * 64 bytes = TILE / 16 blocks of 1 KB; block b belongs to wave
+// b / LPW, and lane l lands at byte 16 l of its block.
+template <bool MN, int TILE>
+__device__ __forceinline__ void dload(const Opnd& op, int64_t mn0, int64_t k0, uint16_t* tile,
+                                      int q) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wr = w >> 1, wc = w & 1;
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int chunk = 2 * ks + (lane >> 5);
-    bf16x8_t a[2], b[2];
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      const int row = 64 * wr + 32 * bi + (lane & 31);
-      a[bi] = *reinterpret_cast<const bf16x8_t*>(sp + lds_idx(row, chunk));
-    }
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
-      const int row = 64 * wc + 32 * bj + (lane & 31);
-      b[bj] = *reinterpret_cast<const bf16x8_t*>(sq + lds_idx(row, chunk));
-    }
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
-        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+  const int blk = w * Geo<TILE>::LPW + q;
+  const uint16_t* src;
+  if constexpr (!MN) {  // 16 rows of 64 bytes per block
+    const int row = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    src = op.p + (mn0 + row) * op.ld + k0 + 8 * c;
+  } else {              // 512 / TILE k rows of 2 TILE bytes per block
+    constexpr int CPR = TILE / 8;  // 16-byte chunks per k row
+    const int row = blk * (512 / TILE) + lane / CPR;
+    const int c = (lane % CPR) ^ (2 * (row & 3));
+    src = op.p + (k0 + row) * op.ld + mn0 + 8 * c;
+  }
+  dma16(src, tile + __builtin_amdgcn_readfirstlane(blk) * 512);
+}
+
+// MFMA fragment (32 rows from rowbase, k = 16 sub .. 16 sub + 15) of one operand tile.
+template <bool MN, int TILE>
+__device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase, int sub) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (!MN) {
+    const int row = rowbase + (lane & 31);
+    const int c = (2 * sub + (lane >> 5)) ^ ((row >> 1) & 3);
+    return *reinterpret_cast<const bf16x8_t*>(tile + row * BK + c * 8);
+  } else {
+    const int g = lane >> 4, i = lane & 15;
+    const int m = rowbase + 16 * (g & 1) + 4 * (i & 3);
+    const int k = 16 * sub + 8 * (g >> 1) + (i >> 2);   // + 4 t below; k & 3 == i >> 2
+    const int off = (((m >> 3) ^ (2 * (i >> 2))) << 3) + (m & 4);
+    const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(tile + k * TILE + off));
+    const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(tile + (k + 4) * TILE + off));
+    u32x4 v;
+    v.x = __builtin_bit_cast(u32x2, r0).x;
+    v.y = __builtin_bit_cast(u32x2, r0).y;
+    v.z = __builtin_bit_cast(u32x2, r1).x;
+    v.w = __builtin_bit_cast(u32x2, r1).y;
+    return __builtin_bit_cast(bf16x8_t, v);
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
+template <int NB>
+__device__ __forceinline__ void mfma_block(const bf16x8_t (&fa)[NB], const bf16x8_t (&fb)[NB],
+                                           f32x16_t (&acc)[NB][NB]) {
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < NB; ++bj)
+      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
+}
+
+template <int NB>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][NB]) {
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 }
 
-// acc += P[mp0 : mp0+128, :K] * Q[nq0 : nq0+128, :K]^T   (K a multiple of 64)
-template <bool PMN, bool QMN>
+// acc += P[mp0 : mp0+TILE, :K] * Q[nq0 : nq0+TILE, :K]^T   (K a multiple of 128)
+//
+// Iteration kt (stage kt mod 4 holds K step kt), instruction order pinned:
+//   substep 0: its NB*NB MFMAs; between them the fragment reads of substep 1
+//              and the loads of step kt+3 into stage (kt+3) mod 4 (its last
+//              reader finished before the previous iteration's barrier)
+//   wait for this wave's loads of step kt+1; LDS barrier
+//   substep 1: its MFMAs; between them the fragment reads of substep 0 of step kt+1
+// MFMA blocks are walked column by column, so each B fragment is consumed at
+// least 3 NB MFMAs after it was read.  Loads past the end re-read the last
+// step (never consumed) so the body has no branches.
+template <int TILE, bool PMN, bool QMN>
 __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t mp0, int64_t nq0,
-                                          int64_t K, uint16_t* smem, f32x16_t (&acc)[2][2]) {
-  // buffer k holds P at smem + 2k * kLdsTile and Q right after it
-  u32x4 rp[4], rq[4];
-  gload<PMN>(P, mp0, 0, rp);
-  gload<QMN>(Q, nq0, 0, rq);
-  lstore<PMN>(smem, rp);
-  lstore<QMN>(smem + kLdsTile, rq);
-  __syncthreads();
+                                          int64_t K, uint16_t* smem,
+                                          f32x16_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB]) {
+  using G = Geo<TILE>;
+  constexpr int NB = G::NB;
+  constexpr int LPS = 2 * G::LPW;  // loads per wave per stage
+  const int w = threadIdx.x >> 6;
+  const int rowA = G::WT * (w >> 1), rowB = G::WT * (w & 1);
+  bf16x8_t fa0[NB], fb0[NB], fa1[NB], fb1[NB];
   const int64_t kt_n = K / BK;
+  auto stage = [&](int64_t kt) { return smem + static_cast<int>(kt & (kStages - 1)) * (2 * G::TE); };
+  auto load = [&](int64_t kt, int part) {  // part < LPW: P blocks, else Q blocks
+    const int64_t k0 = (kt < kt_n ? kt : kt_n - 1) * BK;
+    uint16_t* st = stage(kt);
+    if (part < G::LPW) dload<PMN, TILE>(P, mp0, k0, st, part);
+    else dload<QMN, TILE>(Q, nq0, k0, st + G::TE, part - G::LPW);
+  };
+#pragma unroll
+  for (int kt = 0; kt < 3; ++kt)
+#pragma unroll
+    for (int part = 0; part < LPS; ++part) load(kt, part);
+  vm_wait<2 * LPS>();
+  lds_barrier();
+#pragma unroll
+  for (int b = 0; b < NB; ++b) fa0[b] = frag<PMN, TILE>(smem, rowA + 32 * b, 0);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) fb0[b] = frag<QMN, TILE>(smem + G::TE, rowB + 32 * b, 0);
   for (int64_t kt = 0; kt < kt_n; ++kt) {
-    uint16_t* cur = smem + static_cast<int>(kt & 1) * (2 * kLdsTile);
-    uint16_t* nxt = smem + static_cast<int>((kt + 1) & 1) * (2 * kLdsTile);
-    const bool more = kt + 1 < kt_n;
-    if (more) {
-      gload<PMN>(P, mp0, (kt + 1) * BK, rp);
-      gload<QMN>(Q, nq0, (kt + 1) * BK, rq);
+    const uint16_t* cur = stage(kt);
+#pragma unroll
+    for (int idx = 0; idx < NB * NB; ++idx) {
+      const int bi = idx % NB, bj = idx / NB;
+      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[bi], fb0[bj], acc[bi][bj], 0, 0, 0);
+      if (idx < NB) fa1[idx] = frag<PMN, TILE>(cur, rowA + 32 * idx, 1);
+      else if (idx < 2 * NB) fb1[idx - NB] = frag<QMN, TILE>(cur + G::TE, rowB + 32 * (idx - NB), 1);
+      else if (idx - 2 * NB < LPS) load(kt + 3, idx - 2 * NB);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    mma_step(cur, cur + kLdsTile, acc);
-    if (more) {
-      lstore<PMN>(nxt, rp);
-      lstore<QMN>(nxt + kLdsTile, rq);
+#pragma unroll
+    for (int part = NB * NB - 2 * NB; part < LPS; ++part) {
+      if (part >= 0) load(kt + 3, part);
     }
-    __syncthreads();
+    vm_wait<2 * LPS>();
+    lds_barrier();
+    const uint16_t* nx = stage(kt + 1);
+#pragma unroll
+    for (int idx = 0; idx < NB * NB; ++idx) {
+      const int bi = idx % NB, bj = idx / NB;
+      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[bi], fb1[bj], acc[bi][bj], 0, 0, 0);
+      if (idx < NB) fa0[idx] = frag<PMN, TILE>(nx, rowA + 32 * idx, 0);
+      else if (idx < 2 * NB) fb0[idx - NB] = frag<QMN, TILE>(nx + G::TE, rowB + 32 * (idx - NB), 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  vm_wait<0>();
+  lds_barrier();  // every wave is done with every stage
 }
 
-// Position of accumulator element r of MFMA block (bi, bj) inside the 128 x 128 tile.
+// Position of accumulator element r of MFMA block (bi, bj) inside the tile.
+template <int TILE>
 __device__ __forceinline__ void acc_pos(int bi, int bj, int r, int& row, int& col) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  row = 64 * (w >> 1) + 32 * bi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-  col = 64 * (w & 1) + 32 * bj + (lane & 31);
+  row = Geo<TILE>::WT * (w >> 1) + 32 * bi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  col = Geo<TILE>::WT * (w & 1) + 32 * bj + (lane & 31);
 }
 
 // Symmetric store of a Gram-type tile (ti <= tj): the tile and its mirror.
@@ -393,23 +462,25 @@ __device__ __forceinline__ void acc_pos(int bi, int bj, int r, int& row, int& co
 //   GRAM2 == false:  out = bf16(acc)                          (A = X X^T)
 //   GRAM2 == true:   C = a [row == col] + b A + c acc  (acc = A A), out = bf16(C),
 //                    and out_lo = bf16(C - out) when out_lo is given.
-template <bool GRAM2>
-__device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t* out,
-                                          uint16_t* out_lo, const uint16_t* src, int64_t ld,
-                                          int64_t ti, int64_t tj, float a, float b, float c) {
+template <int TILE, bool GRAM2>
+__device__ __forceinline__ void store_sym(const f32x16_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB],
+                                          uint16_t* out, uint16_t* out_lo, const uint16_t* src,
+                                          int64_t ld, int64_t ti, int64_t tj, float a, float b,
+                                          float c) {
+  constexpr int NB = Geo<TILE>::NB;
   const bool diag = ti == tj;
-  const int64_t r0 = ti * BM, c0 = tj * BN;
+  const int64_t r0 = ti * TILE, c0 = tj * TILE;
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < NB; ++bj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint16_t h[4], l[4];
         int row = 0, col = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc_pos(bi, bj, 4 * g + q, row, col);
+          acc_pos<TILE>(bi, bj, 4 * g + q, row, col);
           float v = acc[bi][bj][4 * g + q];
           if constexpr (GRAM2) {
             const float diag_a = (diag && row == col) ? a : 0.f;
@@ -418,7 +489,7 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t*
           h[q] = f2bf(v);
           l[q] = f2bf(v - bf2f(h[q]));
         }
-        acc_pos(bi, bj, 4 * g, row, col);  // rows row..row+3, one column
+        acc_pos<TILE>(bi, bj, 4 * g, row, col);  // rows row..row+3, one column
         if (!diag) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) gst<uint16_t>(out + (r0 + row + q) * ld + c0 + col, h[q]);
@@ -426,7 +497,7 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t*
           m.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
           m.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
           gst<u32x2>(out + (c0 + col) * ld + r0 + row, m);
-          if (GRAM2 && out_lo) {
+          if (GRAM2 && TILE == kTileSmall && out_lo) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) gst<uint16_t>(out_lo + (r0 + row + q) * ld + c0 + col, l[q]);
             m.x = l[0] | (static_cast<uint32_t>(l[1]) << 16);
@@ -439,7 +510,7 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[2][2], uint16_t*
             if (row + q <= col) {
               gst<uint16_t>(out + (r0 + row + q) * ld + c0 + col, h[q]);
               gst<uint16_t>(out + (c0 + col) * ld + r0 + row + q, h[q]);
-              if (GRAM2 && out_lo) {
+              if (GRAM2 && TILE == kTileSmall && out_lo) {
                 gst<uint16_t>(out_lo + (r0 + row + q) * ld + c0 + col, l[q]);
                 gst<uint16_t>(out_lo + (c0 + col) * ld + r0 + row + q, l[q]);
               }
@@ -469,81 +540,94 @@ __device__ __forceinline__ void decode_full(int64_t u, int64_t tm, int64_t tn, i
   tj = local / gm;
 }
 
-// K3a: A = X X^T for every matrix (upper tiles + mirror)
+// K3a: A = X X^T for every matrix of the launch (upper tiles + mirror)
+template <int TILE>
 __global__ __launch_bounds__(kGemmThreads) void k_gram(const MatDesc* __restrict__ descs,
                                                        const int64_t* __restrict__ prefix, int n,
                                                        int64_t units, int parity) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kLdsTile];
+  using G = Geo<TILE>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * G::TE];
   const int64_t unit = xcd_remap(blockIdx.x, units);
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
   int64_t ti, tj;
-  decode_sym(unit - prefix[i], d.m_pad / BM, ti, tj);
+  decode_sym(unit - prefix[i], d.m_pad / TILE, ti, tj);
   const Opnd X{d.x[parity], d.cols_pad};
-  f32x16_t acc[2][2];
-  zero_acc(acc);
+  f32x16_t acc[G::NB][G::NB];
+  zero_acc<G::NB>(acc);
   if (d.flags & kFlagTall)
-    gemm_tile<true, true>(X, X, ti * BM, tj * BN, d.rows_pad, smem, acc);
+    gemm_tile<TILE, true, true>(X, X, ti * TILE, tj * TILE, d.rows_pad, smem, acc);
   else
-    gemm_tile<false, false>(X, X, ti * BM, tj * BN, d.cols_pad, smem, acc);
-  store_sym<false>(acc, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f);
+    gemm_tile<TILE, false, false>(X, X, ti * TILE, tj * TILE, d.cols_pad, smem, acc);
+  store_sym<TILE, false>(acc, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f);
 }
 
 // K3b: C = a I + b A + c A A  (A symmetric: A A = A A^T, a K-contiguous product).
 // Folding a X into C (X' = C X) keeps the large cancelling terms of the
 // polynomial inside one fp32 sum before the single bf16 rounding.
+template <int TILE>
 __global__ __launch_bounds__(kGemmThreads) void k_gram2(const MatDesc* __restrict__ descs,
                                                         const int64_t* __restrict__ prefix, int n,
                                                         int64_t units, float a, float b, float c) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kLdsTile];
+  using G = Geo<TILE>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * G::TE];
   const int64_t unit = xcd_remap(blockIdx.x, units);
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
   int64_t ti, tj;
-  decode_sym(unit - prefix[i], d.m_pad / BM, ti, tj);
+  decode_sym(unit - prefix[i], d.m_pad / TILE, ti, tj);
   const Opnd A{d.a, d.m_pad};
-  f32x16_t acc[2][2];
-  zero_acc(acc);
-  gemm_tile<false, false>(A, A, ti * BM, tj * BN, d.m_pad, smem, acc);
-  store_sym<true>(acc, d.b, (d.flags & kFlagSplitC) ? d.blo : nullptr, d.a, d.m_pad, ti, tj, a, b, c);
+  f32x16_t acc[G::NB][G::NB];
+  zero_acc<G::NB>(acc);
+  gemm_tile<TILE, false, false>(A, A, ti * TILE, tj * TILE, d.m_pad, smem, acc);
+  // the hi/lo split only exists for short sides <= 128, i.e. in the 128 class
+  uint16_t* lo = (TILE == kTileSmall && (d.flags & kFlagSplitC)) ? d.blo : nullptr;
+  store_sym<TILE, true>(acc, d.b, lo, d.a, d.m_pad, ti, tj, a, b, c);
 }
 
 // K4: X' = C X.  Wide (rows <= cols): X'[i][k] = sum_j C[i][j] X[j][k].
 // Tall: the stored matrix is X^T, so X'^T = X^T C (C symmetric).
 // Split matrices add the low part: X' = C_hi X + C_lo X.
+template <int TILE>
 __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restrict__ descs,
                                                           const int64_t* __restrict__ prefix,
                                                           int n, int64_t units, int parity) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kLdsTile];
+  using G = Geo<TILE>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * G::TE];
   const int64_t unit = xcd_remap(blockIdx.x, units);
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
   int64_t ti, tj;
-  decode_full(unit - prefix[i], d.rows_pad / BM, d.cols_pad / BN, ti, tj);
+  decode_full(unit - prefix[i], d.rows_pad / TILE, d.cols_pad / TILE, ti, tj);
   const uint16_t* x = d.x[parity];
   uint16_t* xn = d.x[parity ^ 1];
   const int64_t ld = d.cols_pad;
-  const bool split = (d.flags & kFlagSplitC) != 0;
-  f32x16_t acc[2][2];
-  zero_acc(acc);
+  // the hi/lo split only exists for short sides <= 128, i.e. in the 128 class
+  const bool split = TILE == kTileSmall && (d.flags & kFlagSplitC) != 0;
+  f32x16_t acc[G::NB][G::NB];
+  zero_acc<G::NB>(acc);
   if (d.flags & kFlagTall) {
-    gemm_tile<false, false>(Opnd{x, ld}, Opnd{d.b, d.m_pad}, ti * BM, tj * BN, d.m_pad, smem, acc);
+    gemm_tile<TILE, false, false>(Opnd{x, ld}, Opnd{d.b, d.m_pad}, ti * TILE, tj * TILE, d.m_pad,
+                                  smem, acc);
     if (split)
-      gemm_tile<false, false>(Opnd{x, ld}, Opnd{d.blo, d.m_pad}, ti * BM, tj * BN, d.m_pad, smem, acc);
+      gemm_tile<TILE, false, false>(Opnd{x, ld}, Opnd{d.blo, d.m_pad}, ti * TILE, tj * TILE,
+                                    d.m_pad, smem, acc);
   } else {
-    gemm_tile<false, true>(Opnd{d.b, d.m_pad}, Opnd{x, ld}, ti * BM, tj * BN, d.m_pad, smem, acc);
+    gemm_tile<TILE, false, true>(Opnd{d.b, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE, d.m_pad,
+                                 smem, acc);
     if (split)
-      gemm_tile<false, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * BM, tj * BN, d.m_pad, smem, acc);
+      gemm_tile<TILE, false, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
+                                   d.m_pad, smem, acc);
   }
-  const int64_t r0 = ti * BM, c0 = tj * BN;
+  const int64_t r0 = ti * TILE, c0 = tj * TILE;
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < G::NB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < G::NB; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         int row, col;
-        acc_pos(bi, bj, r, row, col);
+        acc_pos<TILE>(bi, bj, r, row, col);
         gst<uint16_t>(xn + (r0 + row) * ld + c0 + col, f2bf(acc[bi][bj][r]));
       }
 }
@@ -569,27 +653,42 @@ int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t uni
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_gram(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                void* stream) {
+int launch_gram(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                int parity, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
-  hipLaunchKernelGGL(k_gram, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, units, parity);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tile == 256)
+    hipLaunchKernelGGL(k_gram<256>, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0, st,
+                       d, prefix, n, units, parity);
+  else
+    hipLaunchKernelGGL(k_gram<128>, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0, st,
+                       d, prefix, n, units, parity);
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_gram2(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a, float b,
-                 float c, void* stream) {
+int launch_gram2(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a,
+                 float b, float c, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
-  hipLaunchKernelGGL(k_gram2, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, units, a, b, c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tile == 256)
+    hipLaunchKernelGGL(k_gram2<256>, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0, st,
+                       d, prefix, n, units, a, b, c);
+  else
+    hipLaunchKernelGGL(k_gram2<128>, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0, st,
+                       d, prefix, n, units, a, b, c);
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_xupdate(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                   void* stream) {
+int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
+                   int parity, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
-  hipLaunchKernelGGL(k_xupdate, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, units, parity);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tile == 256)
+    hipLaunchKernelGGL(k_xupdate<256>, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
+                       st, d, prefix, n, units, parity);
+  else
+    hipLaunchKernelGGL(k_xupdate<128>, dim3(static_cast<unsigned>(units)), dim3(kGemmThreads), 0,
+                       st, d, prefix, n, units, parity);
   return static_cast<int>(hipGetLastError());
 }
 

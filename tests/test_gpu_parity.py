@@ -113,7 +113,8 @@ def test_grouped_dispatch_equals_one_by_one_and_is_order_free():
         assert np.array_equal(grouped.param(i), alone[i].param(0)) or rel(grouped.param(i), alone[i].param(0)) <= 1e-7
 
 
-@pytest.mark.parametrize("shape", [(200, 300), (300, 200), (256, 256), (40, 600), (600, 100)])
+@pytest.mark.parametrize("shape", [(200, 300), (300, 200), (256, 256), (40, 600), (600, 100),
+                                   (1024, 1536), (1536, 1024), (1100, 1100)])
 def test_stage_consistency_of_the_gemm_kernels(shape):
     """One iteration (ns = 1) read stage by stage from the workspace: every
     bf16 result is the round-to-nearest of the exact value computed from the
