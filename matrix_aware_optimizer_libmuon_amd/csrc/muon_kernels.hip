@@ -252,8 +252,8 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
 // no register staging, no LDS store instructions): on this chip LDS stores
 // from registers run at about two thirds of the LDS read rate and were the
 // limit.  Four LDS stages; loads run three K steps ahead; one barrier per K
-// step, placed between its two 16-deep MFMA substeps so the fragments of
-// the next step are read while the second substep's MFMAs run.
+// step, placed between its two 16-deep MFMA substeps so the fragments of the
+// next step are read while the second substep's MFMAs run.
 //
 // An operand is "K-contiguous" (element (mn, k) at p[mn * ld + k]) or
 // "MN-contiguous" (element (mn, k) at p[k * ld + mn]).
@@ -382,20 +382,30 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][NB]) {
 //
 // Iteration kt (stage kt mod 4 holds K step kt), instruction order pinned:
 //   substep 0: its NB*NB MFMAs; between them the fragment reads of substep 1
-//              and the loads of step kt+3 into stage (kt+3) mod 4 (its last
-//              reader finished before the previous iteration's barrier)
+//              and half of the loads of step kt+3 into stage (kt+3) mod 4
+//              (its last reader finished before the previous barrier)
 //   wait for this wave's loads of step kt+1; LDS barrier
-//   substep 1: its MFMAs; between them the fragment reads of substep 0 of step kt+1
-// MFMA blocks are walked column by column, so each B fragment is consumed at
-// least 3 NB MFMAs after it was read.  Loads past the end re-read the last
-// step (never consumed) so the body has no branches.
-template <int TILE, bool PMN, bool QMN>
+//   substep 1: its MFMAs; between them the fragment reads of substep 0 of
+//              step kt+1 and the other half of the loads of step kt+3
+// The loads are spread one per two MFMAs: issued in bursts they back up the
+// CU's vector memory pipe, and a wave whose load cannot issue cannot issue
+// its next MFMA either.  MFMA blocks are walked column by column, so each B
+// fragment is consumed at least 3 NB MFMAs after it was read.  Loads past
+// the end re-read the last step (never consumed): the body has no branches.
+//
+// SWAP = true accumulates the transposed blocks (MFMA operands exchanged), so
+// each lane ends up holding four consecutive output columns of one row.
+template <int TILE, bool PMN, bool QMN, bool SWAP = false>
 __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t mp0, int64_t nq0,
                                           int64_t K, uint16_t* smem,
                                           f32x16_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB]) {
   using G = Geo<TILE>;
   constexpr int NB = G::NB;
-  constexpr int LPS = 2 * G::LPW;  // loads per wave per stage
+  constexpr int LPS = 2 * G::LPW;       // loads per wave per stage
+  constexpr int HALF = LPS / 2;         // loads per substep
+  // MFMA slot of load j inside a substep (after the 2 NB fragment reads), or
+  // -1 when the substep is too short and the load goes after its MFMAs
+  constexpr int FIRST = 2 * NB + 1;
   const int w = threadIdx.x >> 6;
   const int rowA = G::WT * (w >> 1), rowB = G::WT * (w & 1);
   bf16x8_t fa0[NB], fb0[NB], fa1[NB], fb1[NB];
@@ -407,11 +417,15 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
     if (part < G::LPW) dload<PMN, TILE>(P, mp0, k0, st, part);
     else dload<QMN, TILE>(Q, nq0, k0, st + G::TE, part - G::LPW);
   };
+  auto mfma = [&](const bf16x8_t (&fa)[NB], const bf16x8_t (&fb)[NB], int bi, int bj) {
+    acc[bi][bj] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[bj], fa[bi], acc[bi][bj], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
+  };
 #pragma unroll
-  for (int kt = 0; kt < 3; ++kt)
+  for (int kt = 0; kt < kStages - 1; ++kt)
 #pragma unroll
     for (int part = 0; part < LPS; ++part) load(kt, part);
-  vm_wait<2 * LPS>();
+  vm_wait<(kStages - 2) * LPS>();
   lds_barrier();
 #pragma unroll
   for (int b = 0; b < NB; ++b) fa0[b] = frag<PMN, TILE>(smem, rowA + 32 * b, 0);
@@ -419,30 +433,34 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
   for (int b = 0; b < NB; ++b) fb0[b] = frag<QMN, TILE>(smem + G::TE, rowB + 32 * b, 0);
   for (int64_t kt = 0; kt < kt_n; ++kt) {
     const uint16_t* cur = stage(kt);
+    const int64_t kl = kt + kStages - 1;
 #pragma unroll
     for (int idx = 0; idx < NB * NB; ++idx) {
-      const int bi = idx % NB, bj = idx / NB;
-      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[bi], fb0[bj], acc[bi][bj], 0, 0, 0);
+      mfma(fa0, fb0, idx % NB, idx / NB);
       if (idx < NB) fa1[idx] = frag<PMN, TILE>(cur, rowA + 32 * idx, 1);
       else if (idx < 2 * NB) fb1[idx - NB] = frag<QMN, TILE>(cur + G::TE, rowB + 32 * (idx - NB), 1);
-      else if (idx - 2 * NB < LPS) load(kt + 3, idx - 2 * NB);
+      else if (idx >= FIRST && (idx - FIRST) % 2 == 0 && (idx - FIRST) / 2 < HALF) load(kl, (idx - FIRST) / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int part = NB * NB - 2 * NB; part < LPS; ++part) {
-      if (part >= 0) load(kt + 3, part);
-    }
-    vm_wait<2 * LPS>();
+    for (int j = 0; j < HALF; ++j)
+      if (FIRST + 2 * j >= NB * NB) load(kl, j);
+    // at most: the other half of step kt+3 is not issued yet; steps kt+2 and
+    // the first half of kt+3 may still be in flight
+    vm_wait<LPS + HALF>();
     lds_barrier();
     const uint16_t* nx = stage(kt + 1);
 #pragma unroll
     for (int idx = 0; idx < NB * NB; ++idx) {
-      const int bi = idx % NB, bj = idx / NB;
-      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[bi], fb1[bj], acc[bi][bj], 0, 0, 0);
+      mfma(fa1, fb1, idx % NB, idx / NB);
       if (idx < NB) fa0[idx] = frag<PMN, TILE>(nx, rowA + 32 * idx, 0);
       else if (idx < 2 * NB) fb0[idx - NB] = frag<QMN, TILE>(nx + G::TE, rowB + 32 * (idx - NB), 0);
+      else if (idx >= FIRST && (idx - FIRST) % 2 == 0 && (idx - FIRST) / 2 < HALF) load(kl, HALF + (idx - FIRST) / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = 0; j < HALF; ++j)
+      if (FIRST + 2 * j >= NB * NB) load(kl, HALF + j);
   }
   vm_wait<0>();
   lds_barrier();  // every wave is done with every stage
@@ -456,77 +474,150 @@ __device__ __forceinline__ void acc_pos(int bi, int bj, int r, int& row, int& co
   col = Geo<TILE>::WT * (w & 1) + 32 * bj + (lane & 31);
 }
 
-// Symmetric store of a Gram-type tile (ti <= tj): the tile and its mirror.
-// On a diagonal tile only the upper half (row <= col) is used for both
-// positions, so the stored matrix is exactly symmetric.
+// ---------------------------------------------------------------------------
+// Symmetric tile epilogue (Gram and C = a I + b A + c A A), tile (ti <= tj).
+//
+// The bf16 results are staged in LDS column-major, T[col][row], in units of
+// four rows (8 bytes) whose unit index is XORed with a 4-bit rotation of the
+// column: the 16 columns one staging write covers, and the 4 columns x 4 units
+// one transpose read covers, then fall on distinct banks.  From T:
+//   the mirror tile (rows of A^T) leaves as coalesced 16-byte rows,
+//   the tile itself leaves through transpose reads as 16-byte row pieces.
+// A diagonal tile is first made exactly symmetric in LDS (lower half :=
+// upper half) and written once.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tswz(int col) { return ((col & 3) << 2) | ((col >> 2) & 3); }
+
+template <int TILE>
+__device__ __forceinline__ int tpos(int row, int col) {
+  return col * TILE + ((((row >> 2) ^ tswz(col)) << 2) | (row & 3));
+}
+
+// Write the staged tile T (TILE x TILE, bf16) to out at (r0, c0), and its
+// transpose at (c0, r0) when `mirror`.
+template <int TILE>
+__device__ __forceinline__ void store_staged(const uint16_t* T, uint16_t* out, int64_t ld,
+                                             int64_t r0, int64_t c0, bool mirror) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  if (mirror) {  // out[c0 + col][r0 + 8k .. +7] = T[col][8k .. 8k+7]
+    constexpr int CPL = TILE / 8;
+#pragma unroll 4
+    for (int idx = t; idx < TILE * CPL; idx += kGemmThreads) {
+      const int col = idx / CPL, k = idx % CPL, f = tswz(col);
+      u32x4 v = *reinterpret_cast<const u32x4*>(T + col * TILE + ((2 * k) ^ (f & 14)) * 4);
+      if (f & 1) v = u32x4{v.z, v.w, v.x, v.y};
+      gst<u32x4>(out + (c0 + col) * ld + r0 + 8 * k, v);
+    }
+  }
+  // out[r0 + rb + i][c0 + cb + 8g .. +7] through two transpose reads per lane:
+  // in each 16-lane group, lane i addresses T[cb + 8g + (i >> 2) (+4)][rb + 4 (i & 3)]
+  // and receives T[cb + 8g + j (+4)][rb + i], j = 0..3.
+  const int g = lane >> 4, i = lane & 15;
+  constexpr int NBLK = (TILE / 16) * (TILE / 32);  // blocks of 16 rows x 32 cols
+#pragma unroll 2
+  for (int blk = w; blk < NBLK; blk += 4) {
+    const int rb = (blk / (TILE / 32)) * 16, cb = (blk % (TILE / 32)) * 32;
+    const int col = cb + 8 * g + (i >> 2);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(T + tpos<TILE>(rb + 4 * (i & 3), col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(T + tpos<TILE>(rb + 4 * (i & 3), col + 4)));
+    u32x4 v;
+    v.x = __builtin_bit_cast(u32x2, lo).x;
+    v.y = __builtin_bit_cast(u32x2, lo).y;
+    v.z = __builtin_bit_cast(u32x2, hi).x;
+    v.w = __builtin_bit_cast(u32x2, hi).y;
+    gst<u32x4>(out + (r0 + rb + i) * ld + c0 + cb + 8 * g, v);
+  }
+}
+
+// Make a staged diagonal tile symmetric: position (row, col), row > col, takes
+// the value computed for (col, row).
+template <int TILE>
+__device__ __forceinline__ void symmetrize(uint16_t* T) {
+  for (int idx = threadIdx.x; idx < TILE * TILE; idx += kGemmThreads) {
+    const int row = idx / TILE, col = idx % TILE;
+    if (row > col) T[tpos<TILE>(row, col)] = T[tpos<TILE>(col, row)];
+  }
+}
+
 //   GRAM2 == false:  out = bf16(acc)                          (A = X X^T)
 //   GRAM2 == true:   C = a [row == col] + b A + c acc  (acc = A A), out = bf16(C),
 //                    and out_lo = bf16(C - out) when out_lo is given.
+// `smem` is free (the K loop ended with a barrier) and holds TILE x TILE bf16.
 template <int TILE, bool GRAM2>
 __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB],
-                                          uint16_t* out, uint16_t* out_lo, const uint16_t* src,
-                                          int64_t ld, int64_t ti, int64_t tj, float a, float b,
-                                          float c) {
+                                          uint16_t* smem, uint16_t* out, uint16_t* out_lo,
+                                          const uint16_t* src, int64_t ld, int64_t ti, int64_t tj,
+                                          float a, float b, float c) {
   constexpr int NB = Geo<TILE>::NB;
   const bool diag = ti == tj;
   const int64_t r0 = ti * TILE, c0 = tj * TILE;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rowA = Geo<TILE>::WT * (w >> 1), rowB = Geo<TILE>::WT * (w & 1);
+  for (int pass = 0; pass < ((GRAM2 && out_lo) ? 2 : 1); ++pass) {
 #pragma unroll
-  for (int bi = 0; bi < NB; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < NB; ++bj)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint16_t h[4], l[4];
-        int row = 0, col = 0;
+      for (int bj = 0; bj < NB; ++bj)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc_pos<TILE>(bi, bj, 4 * g + q, row, col);
-          float v = acc[bi][bj][4 * g + q];
-          if constexpr (GRAM2) {
-            const float diag_a = (diag && row == col) ? a : 0.f;
-            v = fmaf(c, v, fmaf(b, bf2f(gld<uint16_t>(src + (r0 + row) * ld + c0 + col)), diag_a));
-          }
-          h[q] = f2bf(v);
-          l[q] = f2bf(v - bf2f(h[q]));
-        }
-        acc_pos<TILE>(bi, bj, 4 * g, row, col);  // rows row..row+3, one column
-        if (!diag) {
+          // rows rr .. rr+3 of column cc (tile coordinates)
+          const int rr = rowA + 32 * bi + 8 * q + 4 * (lane >> 5), cc = rowB + 32 * bj + (lane & 31);
+          float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) gst<uint16_t>(out + (r0 + row + q) * ld + c0 + col, h[q]);
+          for (int e = 0; e < 4; ++e) v[e] = acc[bi][bj][4 * q + e];
+          if constexpr (GRAM2) {
+            // A is symmetric: A[r0+rr+e][c0+cc] = A[c0+cc][r0+rr+e], one 8-byte load
+            const u32x2 av = gld<u32x2>(src + (c0 + cc) * ld + r0 + rr);
+            const float am[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
+                                 __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = fmaf(c, v[e], fmaf(b, am[e], (diag && rr + e == cc) ? a : 0.f));
+          }
+          uint16_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e] = f2bf(v[e]);
+            if (pass == 1) h[e] = f2bf(v[e] - bf2f(h[e]));
+          }
           u32x2 m;
           m.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
           m.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-          gst<u32x2>(out + (c0 + col) * ld + r0 + row, m);
-          if (GRAM2 && TILE == kTileSmall && out_lo) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) gst<uint16_t>(out_lo + (r0 + row + q) * ld + c0 + col, l[q]);
-            m.x = l[0] | (static_cast<uint32_t>(l[1]) << 16);
-            m.y = l[2] | (static_cast<uint32_t>(l[3]) << 16);
-            gst<u32x2>(out_lo + (c0 + col) * ld + r0 + row, m);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (row + q <= col) {
-              gst<uint16_t>(out + (r0 + row + q) * ld + c0 + col, h[q]);
-              gst<uint16_t>(out + (c0 + col) * ld + r0 + row + q, h[q]);
-              if (GRAM2 && TILE == kTileSmall && out_lo) {
-                gst<uint16_t>(out_lo + (r0 + row + q) * ld + c0 + col, l[q]);
-                gst<uint16_t>(out_lo + (c0 + col) * ld + r0 + row + q, l[q]);
-              }
-            }
-          }
+          *reinterpret_cast<u32x2*>(smem + tpos<TILE>(rr, cc)) = m;
         }
-      }
+    lds_barrier();
+    if (diag) {
+      symmetrize<TILE>(smem);
+      lds_barrier();
+    }
+    store_staged<TILE>(smem, pass == 0 ? out : out_lo, ld, r0, c0, !diag);
+    lds_barrier();
+  }
 }
 
+// Upper-triangle tile u of a t x t tile grid -> (ti <= tj).  Tiles are
+// walked in bands of 8 tile rows, column by column inside a band, so the
+// tiles in flight on one XCD form compact blocks that share operand rows
+// and columns in its L2.
 __device__ __forceinline__ void decode_sym(int64_t u, int64_t t, int64_t& ti, int64_t& tj) {
-  ti = 0;
-  while (u >= t - ti) {
-    u -= t - ti;
-    ++ti;
+  constexpr int64_t GM = 8;
+  int64_t lo = 0;
+  for (;;) {
+    const int64_t hi = lo + GM < t ? lo + GM : t;
+    const int64_t band = (hi - lo) * t - (lo + hi - 1) * (hi - lo) / 2;
+    if (u < band || hi == t) break;
+    u -= band;
+    lo = hi;
   }
-  tj = ti + u;
+  const int64_t hi = lo + GM < t ? lo + GM : t;
+  for (tj = lo;; ++tj) {
+    const int64_t rows = (tj < hi - 1 ? tj : hi - 1) - lo + 1;
+    if (u < rows || tj == t - 1) break;
+    u -= rows;
+  }
+  ti = lo + u;
 }
 
 __device__ __forceinline__ void decode_full(int64_t u, int64_t tm, int64_t tn, int64_t& ti,
@@ -559,7 +650,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gram(const MatDesc* __restrict
     gemm_tile<TILE, true, true>(X, X, ti * TILE, tj * TILE, d.rows_pad, smem, acc);
   else
     gemm_tile<TILE, false, false>(X, X, ti * TILE, tj * TILE, d.cols_pad, smem, acc);
-  store_sym<TILE, false>(acc, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f);
+  store_sym<TILE, false>(acc, smem, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f);
 }
 
 // K3b: C = a I + b A + c A A  (A symmetric: A A = A A^T, a K-contiguous product).
@@ -582,7 +673,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gram2(const MatDesc* __restric
   gemm_tile<TILE, false, false>(A, A, ti * TILE, tj * TILE, d.m_pad, smem, acc);
   // the hi/lo split only exists for short sides <= 128, i.e. in the 128 class
   uint16_t* lo = (TILE == kTileSmall && (d.flags & kFlagSplitC)) ? d.blo : nullptr;
-  store_sym<TILE, true>(acc, d.b, lo, d.a, d.m_pad, ti, tj, a, b, c);
+  store_sym<TILE, true>(acc, smem, d.b, lo, d.a, d.m_pad, ti, tj, a, b, c);
 }
 
 // K4: X' = C X.  Wide (rows <= cols): X'[i][k] = sum_j C[i][j] X[j][k].
@@ -607,28 +698,33 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
   f32x16_t acc[G::NB][G::NB];
   zero_acc<G::NB>(acc);
   if (d.flags & kFlagTall) {
-    gemm_tile<TILE, false, false>(Opnd{x, ld}, Opnd{d.b, d.m_pad}, ti * TILE, tj * TILE, d.m_pad,
-                                  smem, acc);
+    gemm_tile<TILE, false, false, true>(Opnd{x, ld}, Opnd{d.b, d.m_pad}, ti * TILE, tj * TILE,
+                                        d.m_pad, smem, acc);
     if (split)
-      gemm_tile<TILE, false, false>(Opnd{x, ld}, Opnd{d.blo, d.m_pad}, ti * TILE, tj * TILE,
-                                    d.m_pad, smem, acc);
+      gemm_tile<TILE, false, false, true>(Opnd{x, ld}, Opnd{d.blo, d.m_pad}, ti * TILE, tj * TILE,
+                                          d.m_pad, smem, acc);
   } else {
-    gemm_tile<TILE, false, true>(Opnd{d.b, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE, d.m_pad,
-                                 smem, acc);
+    gemm_tile<TILE, false, true, true>(Opnd{d.b, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
+                                       d.m_pad, smem, acc);
     if (split)
-      gemm_tile<TILE, false, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
-                                   d.m_pad, smem, acc);
+      gemm_tile<TILE, false, true, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
+                                         d.m_pad, smem, acc);
   }
-  const int64_t r0 = ti * TILE, c0 = tj * TILE;
+  // transposed blocks: lane holds row rowA + 32 bi + (lane & 31), columns
+  // rowB + 32 bj + 8 q + 4 (lane >> 5) .. +3  ->  one 8-byte store each
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t r0 = ti * TILE + G::WT * (w >> 1) + (lane & 31);
+  const int64_t c0 = tj * TILE + G::WT * (w & 1) + 4 * (lane >> 5);
 #pragma unroll
   for (int bi = 0; bi < G::NB; ++bi)
 #pragma unroll
     for (int bj = 0; bj < G::NB; ++bj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int row, col;
-        acc_pos<TILE>(bi, bj, r, row, col);
-        gst<uint16_t>(xn + (r0 + row) * ld + c0 + col, f2bf(acc[bi][bj][r]));
+      for (int q = 0; q < 4; ++q) {
+        u32x2 m;
+        m.x = pack2(acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1]);
+        m.y = pack2(acc[bi][bj][4 * q + 2], acc[bi][bj][4 * q + 3]);
+        gst<u32x2>(xn + (r0 + 32 * bi) * ld + c0 + 32 * bj + 8 * q, m);
       }
 }
 
