@@ -29,7 +29,7 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 // workspace plan (a pure function of the shapes)
 //
-//   [ table: MatDesc[n] | 6 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
+//   [ table: MatDesc[n] | 7 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
 //   then, per matrix (all n, skipped ones included):
 //   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | C ] m_pad x m_pad bf16 each,
 //   and [ C_lo ] m_pad x m_pad bf16 when the short side is <= kSplitMaxM
@@ -37,7 +37,7 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // prefix arrays of the table: element chunks (flat / padded) over all active
 // matrices, then symmetric and full tile counts per tile class
 enum { kPreFlat = 0, kPrePad = 1, kPreSymBig = 2, kPreFullBig = 3, kPreSymSmall = 4,
-       kPreFullSmall = 5, kNumPrefix = 6 };
+       kPreFullSmall = 5, kPreRows = 6, kNumPrefix = 7 };
 
 int tile_class(int64_t r, int64_t c) { return std::min(r, c) >= kBigMinM ? kTileBig : kTileSmall; }
 
@@ -50,7 +50,7 @@ struct MatPlan {
 
 struct Plan {
   int64_t n = 0;
-  size_t desc_off = 0, prefix_off[kNumPrefix] = {0, 0, 0, 0, 0, 0}, nrm2_off = 0, table_bytes = 0;
+  size_t desc_off = 0, prefix_off[kNumPrefix] = {}, nrm2_off = 0, table_bytes = 0;
   size_t total = 0;
   std::vector<MatPlan> mats;
 };
@@ -219,7 +219,7 @@ struct Table {
   std::vector<unsigned char> bytes;
   int n_active = 0;
   int n_big = 0;                      // descriptors [0, n_big) are 256-tile matrices
-  int64_t units[kNumPrefix] = {0, 0, 0, 0, 0, 0};
+  int64_t units[kNumPrefix] = {};
 };
 
 bool finite(float x) { return std::isfinite(x); }
@@ -256,7 +256,7 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
   int64_t* pre[kNumPrefix];
   for (int k = 0; k < kNumPrefix; ++k)
     pre[k] = reinterpret_cast<int64_t*>(t.bytes.data() + plan.prefix_off[k]);
-  int64_t acc[kNumPrefix] = {0, 0, 0, 0, 0, 0};
+  int64_t acc[kNumPrefix] = {};
   int a = 0;
   for (int pass = 0; pass < 2; ++pass) {
     const int want = pass == 0 ? kTileBig : kTileSmall;
@@ -283,14 +283,18 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
       d.n_pad = static_cast<int32_t>(m.n_pad);
       if (m.tall) d.flags |= kFlagTall;
       if (m.split) d.flags |= kFlagSplitC;
+      // row groups of about kChunk elements for the normalise / apply passes
+      d.rg_pad = static_cast<int32_t>(std::max<int64_t>(1, kChunk / m.cols_pad));
+      d.rg = static_cast<int32_t>(std::max<int64_t>(1, kChunk / m.cols));
       desc[a] = d;
       const int64_t flat = m.rows * m.cols;
-      const int64_t padded = m.rows_pad * m.cols_pad;
       const int64_t t_side = m.m_pad / m.tile;
       pre[kPreFlat][a] = acc[kPreFlat];
       acc[kPreFlat] += (flat + kChunk - 1) / kChunk;
       pre[kPrePad][a] = acc[kPrePad];
-      acc[kPrePad] += (padded + kChunk - 1) / kChunk;
+      acc[kPrePad] += (m.rows_pad + d.rg_pad - 1) / d.rg_pad;
+      pre[kPreRows][a] = acc[kPreRows];
+      acc[kPreRows] += (m.rows + d.rg - 1) / d.rg;
       pre[sym][local] = acc[sym];
       acc[sym] += t_side * (t_side + 1) / 2;
       pre[full][local] = acc[full];
@@ -304,6 +308,7 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
   }
   pre[kPreFlat][a] = acc[kPreFlat];
   pre[kPrePad][a] = acc[kPrePad];
+  pre[kPreRows][a] = acc[kPreRows];
   for (int k = 0; k < kNumPrefix; ++k) t.units[k] = acc[k];
 }
 
@@ -353,7 +358,7 @@ int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float l
     if (rc) return rc;
   }
   rc = timed(kPhaseApply, stream, [&] {
-    return launch_apply(d, pre[kPreFlat], n, t.units[kPreFlat], ns_steps & 1, lr, wd, ortho ? 1 : 0, s);
+    return launch_apply(d, pre[kPreRows], n, t.units[kPreRows], ns_steps & 1, lr, wd, ortho ? 1 : 0, s);
   });
   return rc;
 }

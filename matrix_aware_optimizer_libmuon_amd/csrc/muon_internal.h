@@ -66,7 +66,8 @@ struct alignas(16) MatDesc {
   int32_t rows_pad, cols_pad, m_pad, n_pad;
   uint32_t flags;
   float scale;           // update scale s
-  int32_t reserved[2];
+  int32_t rg_pad;        // rows per work unit of the normalise pass (over rows_pad)
+  int32_t rg;            // rows per work unit of the apply pass (over rows)
 };
 static_assert(sizeof(MatDesc) == 128, "descriptor size");
 

@@ -124,9 +124,39 @@ __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
   const int64_t begin = (unit - prefix[i]) * kChunk;
   const int64_t end = begin + kChunk < total ? begin + kChunk : total;
   const bool gbf = (d.flags & kFlagGradBf16) != 0;
+  constexpr int S = kEwThreads * 8;  // elements per block-wide vector step
   float acc = 0.f;
   if (d.flags & kFlagVecFlat) {
-    for (int64_t e = begin + threadIdx.x * 8; e < end; e += kEwThreads * 8) {
+    int64_t e = begin + threadIdx.x * 8;
+    // two 8-element vectors in flight per thread
+    for (; e + S < end; e += 2 * S) {
+      float g0[8], g1[8];
+      load8_src(d.grad, gbf, e, g0);
+      load8_src(d.grad, gbf, e + S, g1);
+      if (norm_only) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf(g0[j], g0[j], fmaf(g1[j], g1[j], acc));
+      } else {
+        f32x4 m0 = gld<f32x4>(d.mom + e), m1 = gld<f32x4>(d.mom + e + 4);
+        f32x4 m2 = gld<f32x4>(d.mom + e + S), m3 = gld<f32x4>(d.mom + e + S + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          m0[j] = fmaf(mu, m0[j], omu * g0[j]);
+          m1[j] = fmaf(mu, m1[j], omu * g0[4 + j]);
+          m2[j] = fmaf(mu, m2[j], omu * g1[j]);
+          m3[j] = fmaf(mu, m3[j], omu * g1[4 + j]);
+          acc = fmaf(m0[j], m0[j], acc);
+          acc = fmaf(m1[j], m1[j], acc);
+          acc = fmaf(m2[j], m2[j], acc);
+          acc = fmaf(m3[j], m3[j], acc);
+        }
+        gst<f32x4>(d.mom + e, m0);
+        gst<f32x4>(d.mom + e + 4, m1);
+        gst<f32x4>(d.mom + e + S, m2);
+        gst<f32x4>(d.mom + e + S + 4, m3);
+      }
+    }
+    if (e < end) {
       float g[8];
       load8_src(d.grad, gbf, e, g);
       if (norm_only) {
@@ -161,8 +191,30 @@ __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
   if (threadIdx.x == 0) unsafeAtomicAdd(d.nrm2, s);
 }
 
+// Walks a row-major block of rows [r0, r1) x [0, w) in steps of `step`
+// elements per thread, keeping (row, col) without a division per step.
+struct RowWalk {
+  int64_t r, c;
+  int sr, sc, w;
+  __device__ RowWalk(int64_t r0, int first, int step, int width) : w(width) {
+    r = r0 + first / width;
+    c = first % width;
+    sr = step / width;
+    sc = step % width;
+  }
+  __device__ void next() {
+    r += sr;
+    c += sc;
+    if (c >= w) {
+      c -= w;
+      ++r;
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
-// K2: X0 = bf16(M / (||M|| + eps)) into the zero-padded rows_pad x cols_pad buffer
+// K2: X0 = bf16(M / (||M|| + eps)) into the zero-padded rows_pad x cols_pad buffer.
+// One work unit = rg_pad padded rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kEwThreads) void k_normalize(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, float eps) {
@@ -173,14 +225,16 @@ __global__ __launch_bounds__(kEwThreads) void k_normalize(
   const void* src = ortho ? d.grad : static_cast<const void*>(d.mom);
   const bool sbf = ortho && (d.flags & kFlagGradBf16);
   const float inv = static_cast<float>(1.0 / (sqrt(gld<double>(d.nrm2)) + static_cast<double>(eps)));
-  const int64_t cp = d.cols_pad;
-  const int64_t total = static_cast<int64_t>(d.rows_pad) * cp;
-  const int64_t begin = (unit - prefix[i]) * kChunk;
-  const int64_t end = begin + kChunk < total ? begin + kChunk : total;
+  const int cp = d.cols_pad;
+  const int64_t r0 = (unit - prefix[i]) * d.rg_pad;
+  const int64_t r1 = r0 + d.rg_pad < d.rows_pad ? r0 + d.rg_pad : d.rows_pad;
+  const int64_t count = (r1 - r0) * cp;
   const bool vec = (d.flags & kFlagVecRows) != 0;
   uint16_t* x0 = d.x[0];
-  for (int64_t e = begin + threadIdx.x * 8; e < end; e += kEwThreads * 8) {
-    const int64_t r = e / cp, c0 = e - r * cp;
+  constexpr int S = kEwThreads * 8;
+  RowWalk p(r0, threadIdx.x * 8, S, cp);
+  for (int64_t e = threadIdx.x * 8; e < count; e += S, p.next()) {
+    const int64_t r = p.r, c0 = p.c;
     float v[8];
     if (r < d.rows && vec && c0 + 8 <= d.cols) {
       load8_src(src, sbf, r * d.cols + c0, v);
@@ -192,12 +246,13 @@ __global__ __launch_bounds__(kEwThreads) void k_normalize(
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = pack2(v[2 * j] * inv, v[2 * j + 1] * inv);
-    gst<u32x4>(x0 + e, o);
+    gst<u32x4>(x0 + r * cp + c0, o);
   }
 }
 
 // ---------------------------------------------------------------------------
-// K5: p <- p (1 - lr wd) - lr s O    (export_only: out <- O, unpadded)
+// K5: p <- p (1 - lr wd) - lr s O    (export_only: out <- O, unpadded).
+// One work unit = rg rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kEwThreads) void k_apply(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, int parity,
@@ -205,21 +260,24 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
   const int64_t unit = blockIdx.x;
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
-  const int64_t total = d.rows * d.cols;
-  const int64_t begin = (unit - prefix[i]) * kChunk;
-  const int64_t end = begin + kChunk < total ? begin + kChunk : total;
   const uint16_t* o = d.x[parity];
-  const int64_t cp = d.cols_pad, cols = d.cols;
+  const int64_t cp = d.cols_pad;
+  const int cols = static_cast<int>(d.cols);
+  const int64_t r0 = (unit - prefix[i]) * d.rg;
+  const int64_t r1 = r0 + d.rg < d.rows ? r0 + d.rg : d.rows;
+  const int64_t count = (r1 - r0) * cols;
   const float decay = 1.0f - lr * wd;
   const float step = lr * d.scale;
   if (d.flags & kFlagVecRows) {
-    for (int64_t e = begin + threadIdx.x * 8; e < end; e += kEwThreads * 8) {
-      const int64_t r = e / cols, c = e - r * cols;
+    constexpr int S = kEwThreads * 8;
+    RowWalk p(r0, threadIdx.x * 8, S, cols);
+    for (int64_t e = threadIdx.x * 8; e < count; e += S, p.next()) {
+      const int64_t r = p.r, c = p.c, g = r * cols + c;
       const u32x4 q = gld<u32x4>(o + r * cp + c);
       if (export_only) {
-        gst<u32x4>(d.out + e, q);
+        gst<u32x4>(d.out + g, q);
       } else {
-        f32x4 p0 = gld<f32x4>(d.param + e), p1 = gld<f32x4>(d.param + e + 4);
+        f32x4 p0 = gld<f32x4>(d.param + g), p1 = gld<f32x4>(d.param + g + 4);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           p0[2 * j] = fmaf(-step, __uint_as_float(q[j] << 16), p0[2 * j] * decay);
@@ -227,16 +285,17 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
           p1[2 * j] = fmaf(-step, __uint_as_float(q[2 + j] << 16), p1[2 * j] * decay);
           p1[2 * j + 1] = fmaf(-step, __uint_as_float(q[2 + j] & 0xffff0000u), p1[2 * j + 1] * decay);
         }
-        gst<f32x4>(d.param + e, p0);
-        gst<f32x4>(d.param + e + 4, p1);
+        gst<f32x4>(d.param + g, p0);
+        gst<f32x4>(d.param + g + 4, p1);
       }
     }
   } else {
-    for (int64_t e = begin + threadIdx.x; e < end; e += kEwThreads) {
-      const int64_t r = e / cols, c = e - r * cols;
+    RowWalk p(r0, threadIdx.x, kEwThreads, cols);
+    for (int64_t e = threadIdx.x; e < count; e += kEwThreads, p.next()) {
+      const int64_t r = p.r, c = p.c, g = r * cols + c;
       const uint16_t q = gld<uint16_t>(o + r * cp + c);
-      if (export_only) gst<uint16_t>(d.out + e, q);
-      else gst<float>(d.param + e, fmaf(-step, bf2f(q), gld<float>(d.param + e) * decay));
+      if (export_only) gst<uint16_t>(d.out + g, q);
+      else gst<float>(d.param + g, fmaf(-step, bf2f(q), gld<float>(d.param + g) * decay));
     }
   }
 }
