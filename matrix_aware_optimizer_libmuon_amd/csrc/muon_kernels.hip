@@ -303,33 +303,36 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
 // ---------------------------------------------------------------------------
 // Newton-Schulz GEMM engine on bf16 MFMA (v_mfma_f32_32x32x16_bf16)
 //
-// Output tile TILE x TILE (128 or 256), K step 32, 4 waves in a 2 x 2 grid,
+// Output tile TILE x TILE (128 or 256), K step 64, 4 waves in a 2 x 2 grid,
 // each wave (TILE/2) x (TILE/2) = NB x NB MFMA blocks of 32 x 32 with fp32
 // accumulators (256 of them per lane at TILE = 256, held in AGPRs).
 //
-// Operand tiles go straight from global memory into LDS (16 bytes per lane,
-// no register staging, no LDS store instructions): on this chip LDS stores
-// from registers run at about two thirds of the LDS read rate and were the
-// limit.  Four LDS stages; loads run three K steps ahead; one barrier per K
-// step, placed between its two 16-deep MFMA substeps so the fragments of the
-// next step are read while the second substep's MFMAs run.
+// Operand tiles are loaded 16 bytes per lane into registers one K step
+// ahead and stored into a double-buffered LDS; with K step 64 every global
+// load covers whole 128-byte lines (K-contiguous rows are 128 bytes).  Each
+// K step is four 16-deep MFMA substeps; the fragments of the next substep
+// are read while the current one's MFMAs run.  Substep 0 stores the P part
+// of the next step and loads the P part of the step after; substep 1 does
+// the same for Q; one LDS barrier, before substep 3, publishes the next
+// step (substep 3 reads its first fragments).
 //
 // An operand is "K-contiguous" (element (mn, k) at p[mn * ld + k]) or
 // "MN-contiguous" (element (mn, k) at p[k * ld + mn]).
-//   K-contiguous tiles sit in LDS as [mn][32 k] (64-byte rows); fragments
+//   K-contiguous tiles sit in LDS as [mn][64 k] (128-byte rows); fragments
 //     are 16-byte reads; the 16-byte chunk c of row r is stored at
-//     c ^ ((r >> 1) & 3), which spreads the 8 rows read per cycle over all
-//     banks.
+//     c ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes and serves 16
+//     lanes of a 16-byte access per cycle: the 16 rows one fragment read
+//     touches per cycle then cover all banks once (rows of equal parity
+//     share bank offsets and differ in the XOR term).
 //   MN-contiguous tiles keep their memory layout, [k][TILE mn]; fragments
 //     are assembled by the LDS transpose read (ds_read_b64_tr_b16: in each
 //     16-lane group, lane 4a + b receives element b of the 8-byte blocks
 //     addressed by lanes a, a + 4, a + 8, a + 12), so the transpose of a tall
-//     matrix is never materialised, not even in registers.  The 16-byte
-//     chunk c of k row r is stored at c ^ (2 (r & 3)): the four k rows one
-//     transpose read touches then hit distinct banks.
+//     matrix is never materialised.  The 16-byte chunk c of k row r is
+//     stored at c ^ (2 (r & 3)).
 // ---------------------------------------------------------------------------
-constexpr int BK = 32;
-constexpr int kStages = 4;
+constexpr int BK = 64;
+constexpr int kStages = 2;
 
 template <int TILE>
 struct Geo {
@@ -337,7 +340,7 @@ struct Geo {
   static constexpr int WT = TILE / 2;      // wave tile
   static constexpr int NB = WT / 32;       // 32x32 MFMA blocks per wave side
   static constexpr int TE = TILE * BK;     // bf16 elements of one staged operand tile
-  static constexpr int LPW = TILE / 64;    // 1 KB direct loads per wave per operand tile
+  static constexpr int LPT = TILE / 32;    // 16-byte loads per thread per operand tile
   static constexpr int LDS = kStages * 2 * TE * 2;  // bytes
 };
 
@@ -347,7 +350,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most N global -> LDS loads of this wave are in flight.
+// Wait until at most N global loads of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -358,38 +361,44 @@ struct Opnd {
   int64_t ld;
 };
 
-// Global -> LDS, 16 bytes per lane, without registers.  Written as a one-line
-// asm statement: it writes only LDS (no register results), and the compiler
-// would otherwise assume every later LDS read may alias these writes and wait
-// for all of them.  Ordering is explicit instead: vm_wait<> on the issuing
-// wave, then an LDS barrier, before any wave reads the stage.
-__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_dst) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) void*)lds_dst));
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0));
-}
-
-// Block q of this wave's share of a TILE x 32 operand tile.  The tile is
-// TILE * 64 bytes = TILE / 16 blocks of 1 KB; block b belongs to wave
-// b / LPW, and lane l lands at byte 16 l of its block.
+// This thread's share of one operand's TILE x 64 tile: LPT pieces of 16
+// bytes.  Piece q of K step kt is read at byte base + kt kstep + q qstride
+// (uniform) + voff (this lane's offset, 32 bits) and stored at LDS element
+// lds + q QL.  Keeping the per-lane part in one 32-bit register lets every
+// load use a scalar base address.
 template <bool MN, int TILE>
-__device__ __forceinline__ void dload(const Opnd& op, int64_t mn0, int64_t k0, uint16_t* tile,
-                                      int q) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int blk = w * Geo<TILE>::LPW + q;
-  const uint16_t* src;
-  if constexpr (!MN) {  // 16 rows of 64 bytes per block
-    const int row = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
-    src = op.p + (mn0 + row) * op.ld + k0 + 8 * c;
-  } else {              // 512 / TILE k rows of 2 TILE bytes per block
-    constexpr int CPR = TILE / 8;  // 16-byte chunks per k row
-    const int row = blk * (512 / TILE) + lane / CPR;
-    const int c = (lane % CPR) ^ (2 * (row & 3));
-    src = op.p + (k0 + row) * op.ld + mn0 + 8 * c;
+struct Feed {
+  static constexpr int CPR = MN ? TILE / 8 : BK / 8;        // 16-byte chunks per LDS row
+  static constexpr int RPQ = kGemmThreads / CPR;            // LDS rows per piece
+  static constexpr int QL = RPQ * (MN ? TILE : BK);         // LDS elements per piece
+  const char* base;
+  int64_t qstride, kstep;
+  uint32_t voff;
+  int lds;
+  __device__ __forceinline__ Feed(const Opnd& op, int64_t mn0) {
+    const int t = threadIdx.x;
+    const int row = t / CPR, c = t % CPR;
+    const int64_t ldb = op.ld * 2;
+    voff = static_cast<uint32_t>(row * ldb + 16 * c);
+    qstride = RPQ * ldb;
+    if constexpr (!MN) {
+      base = reinterpret_cast<const char*>(op.p) + mn0 * ldb;
+      kstep = BK * 2;
+      lds = row * BK + ((c ^ ((row >> 1) & 7)) << 3);
+    } else {
+      base = reinterpret_cast<const char*>(op.p) + mn0 * 2;
+      kstep = BK * ldb;
+      lds = row * TILE + ((c ^ (2 * (row & 3))) << 3);
+    }
   }
-  dma16(src, tile + __builtin_amdgcn_readfirstlane(blk) * 512);
-}
+  __device__ __forceinline__ u32x4 load(int64_t kt, int q) const {
+    const char* b = base + kt * kstep + q * qstride;
+    return gld<u32x4>(reinterpret_cast<const uint16_t*>(b + voff));
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int q, const u32x4& v) const {
+    *reinterpret_cast<u32x4*>(tile + lds + q * QL) = v;
+  }
+};
 
 // MFMA fragment (32 rows from rowbase, k = 16 sub .. 16 sub + 15) of one operand tile.
 template <bool MN, int TILE>
@@ -397,7 +406,7 @@ __device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase, int 
   const int lane = threadIdx.x & 63;
   if constexpr (!MN) {
     const int row = rowbase + (lane & 31);
-    const int c = (2 * sub + (lane >> 5)) ^ ((row >> 1) & 3);
+    const int c = (2 * sub + (lane >> 5)) ^ ((row >> 1) & 7);
     return *reinterpret_cast<const bf16x8_t*>(tile + row * BK + c * 8);
   } else {
     const int g = lane >> 4, i = lane & 15;
@@ -418,16 +427,6 @@ __device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase, int 
 }
 
 template <int NB>
-__device__ __forceinline__ void mfma_block(const bf16x8_t (&fa)[NB], const bf16x8_t (&fb)[NB],
-                                           f32x16_t (&acc)[NB][NB]) {
-#pragma unroll
-  for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-    for (int bj = 0; bj < NB; ++bj)
-      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
-}
-
-template <int NB>
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][NB]) {
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi)
@@ -439,18 +438,18 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][NB]) {
 
 // acc += P[mp0 : mp0+TILE, :K] * Q[nq0 : nq0+TILE, :K]^T   (K a multiple of 128)
 //
-// Iteration kt (stage kt mod 4 holds K step kt), instruction order pinned:
-//   substep 0: its NB*NB MFMAs; between them the fragment reads of substep 1
-//              and half of the loads of step kt+3 into stage (kt+3) mod 4
-//              (its last reader finished before the previous barrier)
-//   wait for this wave's loads of step kt+1; LDS barrier
-//   substep 1: its MFMAs; between them the fragment reads of substep 0 of
-//              step kt+1 and the other half of the loads of step kt+3
-// The loads are spread one per two MFMAs: issued in bursts they back up the
-// CU's vector memory pipe, and a wave whose load cannot issue cannot issue
-// its next MFMA either.  MFMA blocks are walked column by column, so each B
-// fragment is consumed at least 3 NB MFMAs after it was read.  Loads past
-// the end re-read the last step (never consumed): the body has no branches.
+// K step kt lives in LDS buffer kt & 1.  Instruction order inside step kt,
+// pinned with scheduling barriers (one MFMA per slot, NB*NB slots per substep):
+//   substep 0: fragment reads of substep 1; wait for the P registers of
+//              step kt+1, store them into the other buffer (its last reader
+//              finished before the previous barrier), then load P of kt+2
+//   substep 1: fragment reads of substep 2; the same for Q
+//   substep 2: fragment reads of substep 3
+//   LDS barrier: step kt+1 is complete in LDS
+//   substep 3: fragment reads of substep 0 of step kt+1
+// MFMA blocks are walked column by column, so each B fragment is consumed
+// at least 3 NB MFMAs after it was read.  Loads past the end re-read the
+// last step (stored, never consumed): the body has no branches.
 //
 // SWAP = true accumulates the transposed blocks (MFMA operands exchanged), so
 // each lane ends up holding four consecutive output columns of one row.
@@ -459,70 +458,91 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
                                           int64_t K, uint16_t* smem,
                                           f32x16_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB]) {
   using G = Geo<TILE>;
-  constexpr int NB = G::NB;
-  constexpr int LPS = 2 * G::LPW;       // loads per wave per stage
-  constexpr int HALF = LPS / 2;         // loads per substep
-  // MFMA slot of load j inside a substep (after the 2 NB fragment reads), or
-  // -1 when the substep is too short and the load goes after its MFMAs
-  constexpr int FIRST = 2 * NB + 1;
+  constexpr int NB = G::NB, LPT = G::LPT, SLOTS = NB * NB;
+  // per-slot quotas: fragment reads first, then stores, then loads
+  constexpr int RD = (2 * NB + SLOTS - 1) / SLOTS;
   const int w = threadIdx.x >> 6;
   const int rowA = G::WT * (w >> 1), rowB = G::WT * (w & 1);
+  const Feed<PMN, TILE> fp(P, mp0);
+  const Feed<QMN, TILE> fq(Q, nq0);
+  u32x4 gp[LPT], gq[LPT];
   bf16x8_t fa0[NB], fb0[NB], fa1[NB], fb1[NB];
   const int64_t kt_n = K / BK;
-  auto stage = [&](int64_t kt) { return smem + static_cast<int>(kt & (kStages - 1)) * (2 * G::TE); };
-  auto load = [&](int64_t kt, int part) {  // part < LPW: P blocks, else Q blocks
-    const int64_t k0 = (kt < kt_n ? kt : kt_n - 1) * BK;
-    uint16_t* st = stage(kt);
-    if (part < G::LPW) dload<PMN, TILE>(P, mp0, k0, st, part);
-    else dload<QMN, TILE>(Q, nq0, k0, st + G::TE, part - G::LPW);
-  };
+  auto buf = [&](int64_t kt) { return smem + static_cast<int>(kt & 1) * (2 * G::TE); };
   auto mfma = [&](const bf16x8_t (&fa)[NB], const bf16x8_t (&fb)[NB], int bi, int bj) {
     acc[bi][bj] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[bj], fa[bi], acc[bi][bj], 0, 0, 0)
                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
   };
+  // fragment read number r (0 .. 2 NB - 1) of substep `sub` from tile `t`
+  auto rd = [&](bf16x8_t (&fa)[NB], bf16x8_t (&fb)[NB], const uint16_t* t, int sub, int r) {
+    if (r < NB) fa[r] = frag<PMN, TILE>(t, rowA + 32 * r, sub);
+    else fb[r - NB] = frag<QMN, TILE>(t + G::TE, rowB + 32 * (r - NB), sub);
+  };
+
 #pragma unroll
-  for (int kt = 0; kt < kStages - 1; ++kt)
+  for (int q = 0; q < LPT; ++q) gp[q] = fp.load(0, q);
 #pragma unroll
-    for (int part = 0; part < LPS; ++part) load(kt, part);
-  vm_wait<(kStages - 2) * LPS>();
+  for (int q = 0; q < LPT; ++q) gq[q] = fq.load(0, q);
+  vm_wait<0>();
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) fp.store(smem, q, gp[q]);
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) fq.store(smem + G::TE, q, gq[q]);
+  {
+    const int64_t k1 = kt_n > 1 ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) gp[q] = fp.load(k1, q);
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) gq[q] = fq.load(k1, q);
+  }
   lds_barrier();
 #pragma unroll
-  for (int b = 0; b < NB; ++b) fa0[b] = frag<PMN, TILE>(smem, rowA + 32 * b, 0);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) fb0[b] = frag<QMN, TILE>(smem + G::TE, rowB + 32 * b, 0);
+  for (int r = 0; r < 2 * NB; ++r) rd(fa0, fb0, smem, 0, r);
+
+  // store + reload of piece j (P pieces 0 .. LPT-1, then Q pieces) sits in
+  // slot (3 SLOTS j) / (2 LPT) of substeps 0-2: one pair every 1.5 slots
+  auto pair = [&](uint16_t* nxt, int64_t kn, int j) {
+    if (j < LPT) {
+      fp.store(nxt, j, gp[j]);
+      gp[j] = fp.load(kn, j);
+    } else {
+      fq.store(nxt + G::TE, j - LPT, gq[j - LPT]);
+      gq[j - LPT] = fq.load(kn, j - LPT);
+    }
+  };
   for (int64_t kt = 0; kt < kt_n; ++kt) {
-    const uint16_t* cur = stage(kt);
-    const int64_t kl = kt + kStages - 1;
+    const uint16_t* cur = buf(kt);
+    uint16_t* nxt = buf(kt + 1);
+    const int64_t kn = kt + 2 < kt_n ? kt + 2 : kt_n - 1;
 #pragma unroll
-    for (int idx = 0; idx < NB * NB; ++idx) {
-      mfma(fa0, fb0, idx % NB, idx / NB);
-      if (idx < NB) fa1[idx] = frag<PMN, TILE>(cur, rowA + 32 * idx, 1);
-      else if (idx < 2 * NB) fb1[idx - NB] = frag<QMN, TILE>(cur + G::TE, rowB + 32 * (idx - NB), 1);
-      else if (idx >= FIRST && (idx - FIRST) % 2 == 0 && (idx - FIRST) / 2 < HALF) load(kl, (idx - FIRST) / 2);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int sub = 0; sub < 4; ++sub) {
+      if (sub == 3) lds_barrier();  // step kt+1 is complete in LDS
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        if (sub & 1) mfma(fa1, fb1, s % NB, s / NB);
+        else mfma(fa0, fb0, s % NB, s / NB);
+#pragma unroll
+        for (int r = 0; r < RD; ++r) {
+          const int rr = s * RD + r;
+          if (rr < 2 * NB) {
+            if (sub == 0) rd(fa1, fb1, cur, 1, rr);
+            else if (sub == 1) rd(fa0, fb0, cur, 2, rr);
+            else if (sub == 2) rd(fa1, fb1, cur, 3, rr);
+            else rd(fa0, fb0, nxt, 0, rr);
+          }
+        }
+        if (sub < 3) {
+          const int g = sub * SLOTS + s;
+#pragma unroll
+          for (int jj = 0; jj < 2 * LPT; ++jj)
+            if ((jj * 3 * SLOTS) / (2 * LPT) == g) pair(nxt, kn, jj);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-#pragma unroll
-    for (int j = 0; j < HALF; ++j)
-      if (FIRST + 2 * j >= NB * NB) load(kl, j);
-    // at most: the other half of step kt+3 is not issued yet; steps kt+2 and
-    // the first half of kt+3 may still be in flight
-    vm_wait<LPS + HALF>();
-    lds_barrier();
-    const uint16_t* nx = stage(kt + 1);
-#pragma unroll
-    for (int idx = 0; idx < NB * NB; ++idx) {
-      mfma(fa1, fb1, idx % NB, idx / NB);
-      if (idx < NB) fa0[idx] = frag<PMN, TILE>(nx, rowA + 32 * idx, 0);
-      else if (idx < 2 * NB) fb0[idx - NB] = frag<QMN, TILE>(nx + G::TE, rowB + 32 * (idx - NB), 0);
-      else if (idx >= FIRST && (idx - FIRST) % 2 == 0 && (idx - FIRST) / 2 < HALF) load(kl, HALF + (idx - FIRST) / 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < HALF; ++j)
-      if (FIRST + 2 * j >= NB * NB) load(kl, HALF + j);
   }
   vm_wait<0>();
-  lds_barrier();  // every wave is done with every stage
+  lds_barrier();  // every wave is done with every buffer
 }
 
 // Position of accumulator element r of MFMA block (bi, bj) inside the tile.
@@ -591,12 +611,35 @@ __device__ __forceinline__ void store_staged(const uint16_t* T, uint16_t* out, i
 }
 
 // Make a staged diagonal tile symmetric: position (row, col), row > col, takes
-// the value computed for (col, row).
+// the value computed for (col, row).  Works on 4 x 4 blocks: the four 8-byte
+// column pieces of the upper block (b, a) are read, transposed in registers
+// and written as the columns of the lower block (a, b), a > b; a diagonal
+// block keeps its upper half and mirrors it into its lower half.
 template <int TILE>
 __device__ __forceinline__ void symmetrize(uint16_t* T) {
-  for (int idx = threadIdx.x; idx < TILE * TILE; idx += kGemmThreads) {
-    const int row = idx / TILE, col = idx % TILE;
-    if (row > col) T[tpos<TILE>(row, col)] = T[tpos<TILE>(col, row)];
+  constexpr int U = TILE / 4;                 // 4 x 4 blocks per side
+  constexpr int NBLK = U * (U + 1) / 2;       // blocks on or below the diagonal
+  for (int idx = threadIdx.x; idx < NBLK; idx += kGemmThreads) {
+    int a = static_cast<int>((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
+    if (a * (a + 1) / 2 > idx) --a;
+    if ((a + 1) * (a + 2) / 2 <= idx) ++a;
+    const int b = idx - a * (a + 1) / 2;      // b <= a
+    uint16_t u[4][4];                         // u[j][i] = T(4b + i, 4a + j)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(T + tpos<TILE>(4 * b, 4 * a + j));
+      u[j][0] = v.x & 0xffff; u[j][1] = v.x >> 16; u[j][2] = v.y & 0xffff; u[j][3] = v.y >> 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {             // column 4b + i, rows 4a .. 4a + 3
+      uint16_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = (a > b || j > i) ? u[j][i] : u[i][j];
+      u32x2 v;
+      v.x = o[0] | (static_cast<uint32_t>(o[1]) << 16);
+      v.y = o[2] | (static_cast<uint32_t>(o[3]) << 16);
+      *reinterpret_cast<u32x2*>(T + tpos<TILE>(4 * a, 4 * b + i)) = v;
+    }
   }
 }
 
@@ -614,6 +657,25 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[Geo<TILE>::NB][G
   const int64_t r0 = ti * TILE, c0 = tj * TILE;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rowA = Geo<TILE>::WT * (w >> 1), rowB = Geo<TILE>::WT * (w & 1);
+  // GRAM2: every A value the tile needs, loaded up front (one memory round
+  // trip instead of one per block).  A is symmetric, so A[r0+rr+e][c0+cc] =
+  // A[c0+cc][r0+rr+e]: rows rr .. rr+3 of column cc are one 8-byte load.
+  // (At TILE = 128 the loads stay next to their use: the extra registers
+  // would cost the second resident block per CU.)
+  constexpr bool kBatch = GRAM2 && TILE == kTileBig;
+  u32x2 asrc[kBatch ? NB : 1][kBatch ? NB : 1][kBatch ? 4 : 1];
+  if constexpr (kBatch) {
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = rowA + 32 * bi + 8 * q + 4 * (lane >> 5), cc = rowB + 32 * bj + (lane & 31);
+          asrc[bi][bj][q] = gld<u32x2>(src + (c0 + cc) * ld + r0 + rr);
+        }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first use
+  }
   for (int pass = 0; pass < ((GRAM2 && out_lo) ? 2 : 1); ++pass) {
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
@@ -627,8 +689,9 @@ __device__ __forceinline__ void store_sym(const f32x16_t (&acc)[Geo<TILE>::NB][G
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[bi][bj][4 * q + e];
           if constexpr (GRAM2) {
-            // A is symmetric: A[r0+rr+e][c0+cc] = A[c0+cc][r0+rr+e], one 8-byte load
-            const u32x2 av = gld<u32x2>(src + (c0 + cc) * ld + r0 + rr);
+            u32x2 av;
+            if constexpr (kBatch) av = asrc[bi][bj][q];
+            else av = gld<u32x2>(src + (c0 + cc) * ld + r0 + rr);
             const float am[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
                                  __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
 #pragma unroll
@@ -769,11 +832,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
       gemm_tile<TILE, false, true, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
                                          d.m_pad, smem, acc);
   }
-  // transposed blocks: lane holds row rowA + 32 bi + (lane & 31), columns
-  // rowB + 32 bj + 8 q + 4 (lane >> 5) .. +3  ->  one 8-byte store each
+  // Stage the bf16 tile in LDS, row-major with 8-byte units XORed by the row
+  // (unit u of row r at u ^ (r & 31): a staging write, 32 rows at one unit,
+  // then covers all banks), and write it out as whole 16-byte row chunks.
+  // Transposed blocks: lane holds row rowA + 32 bi + (lane & 31), columns
+  // rowB + 32 bj + 8 q + 4 (lane >> 5) .. +3.
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t r0 = ti * TILE + G::WT * (w >> 1) + (lane & 31);
-  const int64_t c0 = tj * TILE + G::WT * (w & 1) + 4 * (lane >> 5);
+  const int rl = G::WT * (w >> 1) + (lane & 31);
+  const int cl = G::WT * (w & 1) + 4 * (lane >> 5);
 #pragma unroll
   for (int bi = 0; bi < G::NB; ++bi)
 #pragma unroll
@@ -783,8 +849,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
         u32x2 m;
         m.x = pack2(acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1]);
         m.y = pack2(acc[bi][bj][4 * q + 2], acc[bi][bj][4 * q + 3]);
-        gst<u32x2>(xn + (r0 + 32 * bi) * ld + c0 + 32 * bj + 8 * q, m);
+        const int r = rl + 32 * bi, u = (cl + 32 * bj + 8 * q) >> 2;
+        *reinterpret_cast<u32x2*>(smem + r * TILE + ((u ^ (r & 31)) << 2)) = m;
       }
+  lds_barrier();
+  constexpr int CPR = TILE / 8;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int idx = threadIdx.x; idx < TILE * CPR; idx += kGemmThreads) {
+    const int r = idx / CPR, ch = idx % CPR;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(smem + r * TILE + (((2 * ch) ^ (r & 31)) << 2));
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(smem + r * TILE + (((2 * ch + 1) ^ (r & 31)) << 2));
+    gst<u32x4>(xn + (ti * TILE + r) * ld + tj * TILE + 8 * ch, u32x4{lo.x, lo.y, hi.x, hi.y});
+  }
 }
 
 // ---------------------------------------------------------------------------
