@@ -167,7 +167,7 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
   }
   if (s.cap < bytes) {
-    if (s.host) hipHostFree(s.host);
+    if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
     const size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);

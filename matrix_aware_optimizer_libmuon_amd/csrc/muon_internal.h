@@ -86,4 +86,19 @@ int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
                  float lr, float wd, int export_only, void* stream);
 
+// per-tile GEMM launchers (muon_gemm256.hip, muon_gemm128.hip)
+int launch_gram_256(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                   void* stream);
+int launch_gram2_256(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a,
+                    float b, float c, void* stream);
+int launch_xupdate_256(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                      void* stream);
+int launch_gram_128(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                   void* stream);
+int launch_gram2_128(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float a,
+                    float b, float c, void* stream);
+int launch_xupdate_128(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
+                      void* stream);
+
+
 }  // namespace muon
