@@ -212,11 +212,16 @@ def main():
         out["ns_tflops"] = flops_step / (ns_ms / 1e3) / 1e12
         out["ns_frac_of_bf16_peak"] = out["ns_tflops"] / BF16_PEAK_TFLOPS
         out["phases"] = per
+        # HBM bytes per launch from the committed rocprofv3 counter profile
+        # (null when the kernels changed since it was taken)
+        from matrix_aware_optimizer_libmuon_amd.profiling import current_traffic
+        for name in per:
+            per[name]["traffic"] = current_traffic(name)
         dom = max(per, key=lambda k: per[k]["avg_launch_ms"] * per[k]["launches_per_step"])
         d = per[dom]
         out["roofline"] = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
                            "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
-                           "traffic": None}
+                           "traffic": d["traffic"]}
 
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4
