@@ -103,6 +103,38 @@ def cpu_baseline(w, target_s: float = 20.0):
                       f"step each (numpy, BLAS threads={cores}); input generation excluded"}
 
 
+def bench_adamw(torch, muon, dev, reps: int = 10):
+    """AdamW branch on the parameters Muon does not take, for the d=4096
+    transformer: token embedding and output head (32000 x 4096 each; the
+    vocabulary size is a reading, the pages give none) and 65 norm weight
+    vectors of 4096, bf16 gradients, fp32 params and moments; HBM-bound, 26
+    algorithmic bytes per element (read p, g, m, v; write p, m, v)."""
+    sizes = [32000 * 4096, 32000 * 4096] + [4096] * 65
+    gen = torch.Generator(device=dev).manual_seed(7)
+    p = [torch.randn(n, device=dev, generator=gen) * 0.02 for n in sizes]
+    g = [(torch.randn(n, device=dev, generator=gen) * 1e-3).to(torch.bfloat16) for n in sizes]
+    m = [torch.zeros(n, device=dev) for n in sizes]
+    v = [torch.zeros(n, device=dev) for n in sizes]
+    ws = muon.alloc_adamw_workspace(len(sizes), dev)
+    steps = [1] * len(sizes)
+    muon.adamw_step(p, g, m, v, steps, workspace=ws)
+    torch.cuda.synchronize()
+    muon.timing_enable(True)
+    muon.timing_read()
+    for r in range(reps):
+        muon.adamw_step(p, g, m, v, [r + 2] * len(sizes), workspace=ws)
+    t = muon.timing_read()["adamw"]
+    muon.timing_enable(False)
+    ms = t["ms"] / t["launches"]
+    elements = sum(sizes)
+    nbytes = elements * 26
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "embedding + head 32000x4096 each, 65 norm vectors of 4096; bf16 grads",
+            "elements": elements, "avg_launch_ms": ms, "bound": "hbm", "achieved": gbs,
+            "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+            "algorithmic_per_launch": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-phase-timing", action="store_true")
+    ap.add_argument("--no-adamw", action="store_true",
+                    help="skip the AdamW-branch measurement (an extra object in the JSON line)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -234,6 +268,9 @@ def main():
         log(f"[bench] copy calibration: {n * 4 / 2**30:.2f} GiB copied")
 
     del params, grads, moms, ws
+    torch.cuda.empty_cache()
+    if not args.no_adamw:
+        out["adamw"] = bench_adamw(torch, muon, dev)
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on a sample ...")

@@ -180,13 +180,54 @@ typedef struct {
 int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index,
                         int ns_steps, muon_workspace_view_t* view);
 
+/* ------------------------------------------------------------------------
+ * AdamW branch: the update the pages pair with Muon for the parameters Muon
+ * does not take (1-D biases and norm weights, embeddings, output heads).
+ * "Muon meets Mamba" (wmrh.cn), section 4.2, method _step_adamw; defaults in
+ * section 4.1 (lr 1e-3, betas (0.9, 0.95), eps 1e-8, weight decay 0.01 shared
+ * with the Muon group).  Per tensor with a gradient, elementwise in fp32:
+ *
+ *   p <- p (1 - lr wd)
+ *   m <- beta1 m + (1 - beta1) g,        v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - (lr / (1 - beta1^t)) m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *
+ * with t the tensor's own step count (the page keeps one per parameter).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float*      param;       /* fp32 [numel], updated in place                        */
+  const void* grad;        /* [numel] of grad_dtype; NULL: the tensor is skipped     */
+                           /* (no decay, no moment update)                           */
+  float*      exp_avg;     /* fp32 [numel] first moment m, in place; caller zero-inits */
+  float*      exp_avg_sq;  /* fp32 [numel] second moment v, in place; caller zero-inits */
+  int64_t     numel;       /* >= 1 elements (any tensor shape, flattened)            */
+  int64_t     step;        /* t of this update, >= 1: the caller keeps the per-tensor */
+                           /* count and increments it before the call                */
+  int32_t     grad_dtype;  /* MUON_F32 or MUON_BF16                                  */
+  int32_t     reserved;    /* must be 0                                              */
+} muon_adamw_tensor_t;
+
+/* Workspace for n_tensors tensors (descriptor table); 0 if n_tensors <= 0. */
+size_t muon_adamw_workspace_bytes(int64_t n_tensors);
+
+/* One AdamW update of every tensor with a gradient, one grouped launch on
+ * `stream`.  Arguments: 0 <= beta1, beta2 < 1, eps >= 0, lr and wd finite.
+ * Same ownership, aliasing and error rules as muon_step: MUON_EINVAL for a
+ * bad argument (numel < 1, step < 1, unknown dtype, missing buffer, reserved
+ * != 0), MUON_EALIAS when any two buffers of the call overlap,
+ * MUON_EWORKSPACE for a missing, small or unaligned workspace, all found
+ * before anything is launched; MUON_EHIP when a launch fails. */
+int muon_adamw_step(const muon_adamw_tensor_t* tensors, int64_t n_tensors, float lr, float beta1,
+                    float beta2, float eps, float wd, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Phase timing with HIP events, for benchmarks.  When enabled, every launch
  * is bracketed by a pair of events on the call's stream.  muon_timing_read()
  * waits for the recorded events, returns the summed milliseconds and launch
  * counts per phase (MUON_PHASES entries each; either pointer may be NULL) and
  * clears the record.  Phases: momentum+norm, normalise+cast, Gram X X^T,
- * Gram A A with the b A + c A^2 epilogue, X update, apply (or export). */
-#define MUON_PHASES 6
+ * Gram A A with the b A + c A^2 epilogue, X update, apply (or export),
+ * AdamW. */
+#define MUON_PHASES 7
 int muon_timing_enable(int on);
 int muon_timing_read(double* ms, int64_t* launches);
 

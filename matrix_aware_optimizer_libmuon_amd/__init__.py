@@ -16,8 +16,8 @@ from typing import Iterable, Sequence
 from . import _lib
 from ._lib import (MUON_BF16, MUON_EALIAS, MUON_EHIP, MUON_EINVAL, MUON_EWORKSPACE,  # noqa: F401
                    MUON_F32, MUON_OK, MUON_SCALE_NONE, MUON_SCALE_SQRT_MAX1, PHASE_NAMES,
-                   LibMuonError, MuonCoeff, MuonMatrix, MuonOrtho, MuonWorkspaceView,
-                   status_string)
+                   LibMuonError, MuonAdamWTensor, MuonCoeff, MuonMatrix, MuonOrtho,
+                   MuonWorkspaceView, status_string)
 
 # Quintic Newton-Schulz coefficients (a, b, c) of the newtonschulz5 routine in
 # "Muon optimizer: matrix-aware LLM" (airosetta.com, implementation section).
@@ -186,6 +186,60 @@ def orthogonalize(inputs: Sequence, outputs: Sequence | None = None, *, ns_steps
                                         _stream_handle(stream, device))
     _lib.check(st, "muon_orthogonalize")
     return outputs
+
+
+# AdamW defaults of the optimizer constructor in "Muon meets Mamba" (wmrh.cn),
+# section 4.1: adamw_lr, adamw_betas, adamw_eps, and the shared weight decay.
+ADAMW_DEFAULTS = {"lr": 1e-3, "betas": (0.9, 0.95), "eps": 1e-8, "wd": 0.01}
+
+
+def adamw_workspace_bytes(n_tensors: int) -> int:
+    return int(_lib.load().muon_adamw_workspace_bytes(int(n_tensors)))
+
+
+def alloc_adamw_workspace(n_tensors: int, device="cuda"):
+    torch = _torch()
+    n = max(adamw_workspace_bytes(n_tensors), 256)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def adamw_step(params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg_sqs: Sequence,
+               steps: Sequence, *, lr: float = 1e-3, betas=(0.9, 0.95), eps: float = 1e-8,
+               wd: float = 0.01, workspace=None, stream=None):
+    """One AdamW update of fp32 GPU tensors of any shape (grads fp32 or bf16,
+    or None to skip), in place, one grouped launch.  ``steps[i]`` is tensor
+    i's step count for this update (>= 1); the caller keeps and increments
+    it.  Returns the workspace used."""
+    torch = _torch()
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == len(steps) == n):
+        raise ValueError("params, grads, exp_avgs, exp_avg_sqs and steps must have the same length")
+    arr = (MuonAdamWTensor * max(1, n))()
+    device = params[0].device if n else torch.device("cuda")
+    for i, (p, g, m, v, t) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs, steps)):
+        for name, x in (("params", p), ("exp_avgs", m), ("exp_avg_sqs", v)):
+            if not x.is_cuda or not x.is_contiguous() or x.dtype != torch.float32:
+                raise ValueError(f"{name}[{i}] must be a contiguous fp32 GPU tensor")
+        if m.shape != p.shape or v.shape != p.shape:
+            raise ValueError(f"moment shapes of tensor {i} differ from the param's")
+        arr[i].param, arr[i].exp_avg, arr[i].exp_avg_sq = p.data_ptr(), m.data_ptr(), v.data_ptr()
+        arr[i].numel = p.numel()
+        arr[i].step = int(t)
+        if g is not None:
+            if not g.is_cuda or not g.is_contiguous() or g.shape != p.shape:
+                raise ValueError(f"grads[{i}] must be a contiguous GPU tensor shaped like its param")
+            arr[i].grad = g.data_ptr()
+            arr[i].grad_dtype = _dtype_code(g)
+    if workspace is None:
+        workspace = alloc_adamw_workspace(n, device)
+    st = _lib.load().muon_adamw_step(arr, n, float(lr), float(betas[0]), float(betas[1]), float(eps),
+                                     float(wd), ctypes.c_void_p(workspace.data_ptr()),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream, device))
+    _lib.check(st, "muon_adamw_step")
+    return workspace
 
 
 def timing_enable(on: bool = True) -> None:

@@ -24,10 +24,12 @@ MUON_BF16 = 1
 MUON_SCALE_NONE = 0
 MUON_SCALE_SQRT_MAX1 = 1
 
-MUON_PHASES = 6
-PHASE_NAMES = ("momentum_norm", "normalize_cast", "gram", "gram2_epilogue", "x_update", "apply")
+MUON_PHASES = 7
+PHASE_NAMES = ("momentum_norm", "normalize_cast", "gram", "gram2_epilogue", "x_update", "apply",
+               "adamw")
 
 EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_orthogonalize", "muon_workspace_view",
+            "muon_adamw_workspace_bytes", "muon_adamw_step",
             "muon_timing_enable", "muon_timing_read", "muon_status_string", "muon_version")
 
 
@@ -45,6 +47,13 @@ class MuonOrtho(ctypes.Structure):
 
 class MuonCoeff(ctypes.Structure):
     _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float)]
+
+
+class MuonAdamWTensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("numel", ctypes.c_int64), ("step", ctypes.c_int64),
+                ("grad_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class MuonWorkspaceView(ctypes.Structure):
@@ -87,6 +96,12 @@ def load() -> ctypes.CDLL:
     lib.muon_workspace_view.argtypes = [P(MuonMatrix), ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         P(MuonWorkspaceView)]
     lib.muon_workspace_view.restype = ctypes.c_int
+    lib.muon_adamw_workspace_bytes.argtypes = [ctypes.c_int64]
+    lib.muon_adamw_workspace_bytes.restype = ctypes.c_size_t
+    lib.muon_adamw_step.argtypes = [P(MuonAdamWTensor), ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+    lib.muon_adamw_step.restype = ctypes.c_int
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_enable.restype = ctypes.c_int
     lib.muon_timing_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]

@@ -496,6 +496,88 @@ int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index
   return MUON_OK;
 }
 
+// ---------------------------------------------------------------------------
+// AdamW branch: [ AdamDesc[n] | prefix int64[n+1] ] in the workspace
+// ---------------------------------------------------------------------------
+size_t muon_adamw_workspace_bytes(int64_t n_tensors) {
+  if (n_tensors <= 0 || n_tensors > (int64_t(1) << 24)) return 0;
+  return align_up(static_cast<size_t>(n_tensors) * sizeof(AdamDesc), kAlign) +
+         align_up(static_cast<size_t>(n_tensors + 1) * sizeof(int64_t), kAlign);
+}
+
+int muon_adamw_step(const muon_adamw_tensor_t* tensors, int64_t n_tensors, float lr, float beta1,
+                    float beta2, float eps, float wd, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return MUON_EINVAL;
+  if (n_tensors > (int64_t(1) << 24)) return MUON_EINVAL;
+  if (!finite(lr) || !finite(wd) || !finite(eps) || !(eps >= 0.0f)) return MUON_EINVAL;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f)) return MUON_EINVAL;
+  if (n_tensors == 0) return MUON_OK;
+  std::vector<std::pair<uintptr_t, uintptr_t>> ranges;
+  int64_t n_active = 0;
+  for (int64_t i = 0; i < n_tensors; ++i) {
+    const muon_adamw_tensor_t& t = tensors[i];
+    if (t.numel < 1 || t.numel > (int64_t(1) << 40) || t.reserved != 0) return MUON_EINVAL;
+    if (!t.grad) continue;
+    if (t.step < 1) return MUON_EINVAL;
+    if (!t.param || !t.exp_avg || !t.exp_avg_sq) return MUON_EINVAL;
+    if (t.grad_dtype != MUON_F32 && t.grad_dtype != MUON_BF16) return MUON_EINVAL;
+    const size_t gsz = t.grad_dtype == MUON_BF16 ? 2 : 4;
+    if (!aligned(t.param, 4) || !aligned(t.exp_avg, 4) || !aligned(t.exp_avg_sq, 4) || !aligned(t.grad, gsz))
+      return MUON_EINVAL;
+    const size_t el = static_cast<size_t>(t.numel);
+    for (const void* b : {static_cast<const void*>(t.param), static_cast<const void*>(t.exp_avg),
+                          static_cast<const void*>(t.exp_avg_sq)})
+      ranges.push_back({reinterpret_cast<uintptr_t>(b), reinterpret_cast<uintptr_t>(b) + el * 4});
+    ranges.push_back({reinterpret_cast<uintptr_t>(t.grad), reinterpret_cast<uintptr_t>(t.grad) + el * gsz});
+    ++n_active;
+  }
+  if (any_overlap(ranges)) return MUON_EALIAS;
+  const size_t need = muon_adamw_workspace_bytes(n_tensors);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return MUON_EWORKSPACE;
+  if (n_active == 0) return MUON_OK;
+  // table: descriptors of the active tensors, then the prefix of their chunk counts
+  const size_t desc_bytes = align_up(static_cast<size_t>(n_tensors) * sizeof(AdamDesc), kAlign);
+  std::vector<unsigned char> bytes(desc_bytes + static_cast<size_t>(n_active + 1) * sizeof(int64_t), 0);
+  AdamDesc* desc = reinterpret_cast<AdamDesc*>(bytes.data());
+  int64_t* pre = reinterpret_cast<int64_t*>(bytes.data() + desc_bytes);
+  int64_t a = 0, units = 0;
+  for (int64_t i = 0; i < n_tensors; ++i) {
+    const muon_adamw_tensor_t& t = tensors[i];
+    if (!t.grad) continue;
+    AdamDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.param = t.param;
+    d.grad = t.grad;
+    d.m = t.exp_avg;
+    d.v = t.exp_avg_sq;
+    d.numel = t.numel;
+    // bias corrections of step t, in double on the host
+    const double c1 = 1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(t.step));
+    const double c2 = 1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(t.step));
+    d.step_size = static_cast<float>(static_cast<double>(lr) / c1);
+    d.inv_sqrt_c2 = static_cast<float>(1.0 / std::sqrt(c2));
+    d.decay = static_cast<float>(1.0 - static_cast<double>(lr) * static_cast<double>(wd));
+    if (t.grad_dtype == MUON_BF16) d.flags |= kFlagGradBf16;
+    if (t.numel % 8 == 0 && aligned(t.param, 16) && aligned(t.exp_avg, 16) && aligned(t.exp_avg_sq, 16) &&
+        aligned(t.grad, 16))
+      d.flags |= kFlagVecFlat;
+    desc[a] = d;
+    pre[a] = units;
+    units += (t.numel + kChunk - 1) / kChunk;
+    ++a;
+  }
+  pre[a] = units;
+  char* ws = static_cast<char*>(workspace);
+  int rc = upload_table(bytes.data(), bytes.size(), ws, stream);
+  if (rc != MUON_OK) return rc;
+  const AdamDesc* dd = reinterpret_cast<const AdamDesc*>(ws);
+  const int64_t* dp = reinterpret_cast<const int64_t*>(ws + desc_bytes);
+  return timed(kPhaseAdamW, stream, [&] {
+    return launch_adamw(dd, dp, static_cast<int>(n_active), units, beta1, beta2, eps, static_cast<void*>(stream));
+  });
+}
+
 int muon_timing_enable(int on) {
   std::lock_guard<std::mutex> lock(g_mu);
   g_timing = on != 0;

@@ -19,8 +19,6 @@ namespace muon {
 constexpr int kTileSmall = 128;
 constexpr int kTileBig = 256;
 constexpr int kBigMinM = 1024;
-// Depth of one K step of the GEMM main loop.
-constexpr int kTileK = 64;
 // Elements handled by one workgroup of the elementwise phases.
 constexpr int kChunk = 16384;
 constexpr int kEwThreads = 256;
@@ -33,7 +31,8 @@ enum Phase : int {
   kPhaseGram2 = 3,
   kPhaseXUpdate = 4,
   kPhaseApply = 5,
-  kNumPhases = 6
+  kPhaseAdamW = 6,
+  kNumPhases = 7
 };
 
 // flags of MatDesc
@@ -71,6 +70,21 @@ struct alignas(16) MatDesc {
 };
 static_assert(sizeof(MatDesc) == 128, "descriptor size");
 
+// One AdamW tensor, as the kernel sees it.  64 bytes.  The per-tensor bias
+// corrections are folded on the host: step_size = lr / (1 - beta1^t),
+// inv_sqrt_c2 = 1 / sqrt(1 - beta2^t), decay = 1 - lr wd.
+struct alignas(16) AdamDesc {
+  float* param;
+  const void* grad;
+  float* m;
+  float* v;
+  int64_t numel;
+  float step_size, inv_sqrt_c2, decay;
+  uint32_t flags;        // kFlagGradBf16, kFlagVecFlat
+  int64_t reserved;
+};
+static_assert(sizeof(AdamDesc) == 64, "AdamW descriptor size");
+
 // kernel launchers (muon_kernels.hip); return hipError_t as int
 int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                          float mu, int norm_only, void* stream);
@@ -85,6 +99,8 @@ int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int
                    int parity, void* stream);
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
                  float lr, float wd, int export_only, void* stream);
+int launch_adamw(const AdamDesc* d, const int64_t* prefix, int n, int64_t units, float beta1,
+                 float beta2, float eps, void* stream);
 
 // per-tile GEMM launchers (muon_gemm256.hip, muon_gemm128.hip)
 int launch_gram_256(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,

@@ -6,6 +6,7 @@
 //   K3b Gram^2    C = a I + b A + c A A      (muon_gemm.h)
 //   K4  X update  X' = C X                   (muon_gemm.h)
 //   K5 apply      p <- p (1 - lr wd) - lr s O (HBM-bound)
+//   AdamW         the branch for the parameters Muon does not take (HBM-bound)
 //
 // Every kernel is one grouped launch over all matrices of a call: workgroup
 // -> (matrix, work unit) by binary search in a per-phase prefix array.
@@ -237,6 +238,65 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
 }
 
 // ---------------------------------------------------------------------------
+// AdamW (the branch for parameters Muon does not take), one work unit =
+// kChunk elements of one tensor, all fp32 math:
+//   p <- p decay;  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+//   p <- p - step_size m / (sqrt(v) inv_sqrt_c2 + eps)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g, float b1,
+                                           float b2, float eps, float decay, float step_size,
+                                           float inv_sqrt_c2) {
+  p *= decay;
+  m = fmaf(b1, m, (1.0f - b1) * g);
+  v = fmaf(b2, v, (1.0f - b2) * (g * g));
+  p = fmaf(-step_size, m / fmaf(sqrtf(v), inv_sqrt_c2, eps), p);
+}
+
+__global__ __launch_bounds__(kEwThreads) void k_adamw(const AdamDesc* __restrict__ descs,
+                                                      const int64_t* __restrict__ prefix, int n,
+                                                      float b1, float b2, float eps) {
+  const int64_t unit = blockIdx.x;
+  const int i = find_matrix(prefix, n, unit);
+  const AdamDesc& d = descs[i];
+  const int64_t begin = (unit - prefix[i]) * kChunk;
+  const int64_t end = begin + kChunk < d.numel ? begin + kChunk : d.numel;
+  const bool gbf = (d.flags & kFlagGradBf16) != 0;
+  const float decay = d.decay, step = d.step_size, isc = d.inv_sqrt_c2;
+  if (d.flags & kFlagVecFlat) {
+    for (int64_t e = begin + threadIdx.x * 8; e < end; e += kEwThreads * 8) {
+      float g[8];
+      load8_src(d.grad, gbf, e, g);
+      f32x4 p0 = gld<f32x4>(d.param + e), p1 = gld<f32x4>(d.param + e + 4);
+      f32x4 m0 = gld<f32x4>(d.m + e), m1 = gld<f32x4>(d.m + e + 4);
+      f32x4 v0 = gld<f32x4>(d.v + e), v1 = gld<f32x4>(d.v + e + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = p0[j], m = m0[j], v = v0[j];
+        adamw_elem(p, m, v, g[j], b1, b2, eps, decay, step, isc);
+        p0[j] = p, m0[j] = m, v0[j] = v;
+        p = p1[j], m = m1[j], v = v1[j];
+        adamw_elem(p, m, v, g[4 + j], b1, b2, eps, decay, step, isc);
+        p1[j] = p, m1[j] = m, v1[j] = v;
+      }
+      gst<f32x4>(d.param + e, p0);
+      gst<f32x4>(d.param + e + 4, p1);
+      gst<f32x4>(d.m + e, m0);
+      gst<f32x4>(d.m + e + 4, m1);
+      gst<f32x4>(d.v + e, v0);
+      gst<f32x4>(d.v + e + 4, v1);
+    }
+  } else {
+    for (int64_t e = begin + threadIdx.x; e < end; e += kEwThreads) {
+      float p = gld<float>(d.param + e), m = gld<float>(d.m + e), v = gld<float>(d.v + e);
+      adamw_elem(p, m, v, load1_src(d.grad, gbf, e), b1, b2, eps, decay, step, isc);
+      gst<float>(d.param + e, p);
+      gst<float>(d.m + e, m);
+      gst<float>(d.v + e, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline int grid_ok(int64_t units) { return units > 0 && units < (int64_t(1) << 31); }
@@ -283,6 +343,14 @@ int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, 
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_apply, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
                      static_cast<hipStream_t>(stream), d, prefix, n, parity, lr, wd, export_only);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_adamw(const AdamDesc* d, const int64_t* prefix, int n, int64_t units, float beta1,
+                 float beta2, float eps, void* stream) {
+  if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
+  hipLaunchKernelGGL(k_adamw, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
+                     static_cast<hipStream_t>(stream), d, prefix, n, beta1, beta2, eps);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -245,6 +245,42 @@ def adhoc_inputs(rows: int, cols: int, grad_dtype: str, seed: int, grad_std: flo
     return MatrixInputs(rows, cols, np.ascontiguousarray(g), bits, p, m)
 
 
+@dataclasses.dataclass
+class AdamWInputs:
+    numel: int
+    grads: list           # float32 arrays (exact values; bf16-representable when bits given)
+    grad_bits: list       # uint16 arrays or None, one per step
+    param: np.ndarray     # float32
+    exp_avg: np.ndarray   # float32
+    exp_avg_sq: np.ndarray
+
+
+def adamw_inputs(numel: int, steps: int, grad_dtype: str, seed: int, grad_std: float = 1.0,
+                 param_std: float = 0.02, warm: bool = False) -> AdamWInputs:
+    """Seeded inputs of one AdamW tensor (flattened): ``steps`` gradients
+    N(0, grad_std) (rounded to bf16 when asked), an N(0, param_std) parameter,
+    and zero moments -- or, with ``warm``, moments of a prior gradient history
+    (first moment N(0, 0.1 grad_std), second |N(0, grad_std^2)|).  Seeds live
+    in their own range (workload key 2000)."""
+    grads, bits = [], []
+    for t in range(steps):
+        g = _normal(_rng(2000, seed, numel, t, ROLE_GRAD), (numel,), grad_std)
+        b = None
+        if grad_dtype == "bf16":
+            b = f32_to_bf16_bits(g)
+            g = bf16_bits_to_f32(b)
+        grads.append(np.ascontiguousarray(g))
+        bits.append(b)
+    p = _normal(_rng(2000, seed, numel, 0, ROLE_PARAM), (numel,), param_std)
+    if warm:
+        m = _normal(_rng(2000, seed, numel, 0, ROLE_MOM), (numel,), 0.1 * grad_std)
+        v = np.abs(_normal(_rng(2000, seed, numel, 1, ROLE_MOM), (numel,), grad_std * grad_std))
+    else:
+        m = np.zeros(numel, dtype=np.float32)
+        v = np.zeros(numel, dtype=np.float32)
+    return AdamWInputs(numel, grads, bits, p, m, v.astype(np.float32))
+
+
 # --------------------------------------------------------------------------
 # device-side draws (benchmark inputs): the same laws as above, drawn by
 # torch's seeded device generator so that the 7.8 G-element workloads do not

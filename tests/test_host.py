@@ -46,6 +46,7 @@ def test_struct_layouts_match_header(lib):
     assert ctypes.sizeof(muon.MuonOrtho) == 40
     assert ctypes.sizeof(muon.MuonCoeff) == 12
     assert ctypes.sizeof(muon.MuonWorkspaceView) == 88
+    assert ctypes.sizeof(muon.MuonAdamWTensor) == 56
 
 
 def test_workspace_plan(lib):
@@ -168,3 +169,45 @@ def test_python_binding_validates_before_calling(lib):
         muon.muon_step([p], [p], [p])                 # CPU tensors are refused
     with pytest.raises(ValueError):
         muon.muon_step([p], [p], [])
+
+
+def _adam(specs):
+    arr = (muon.MuonAdamWTensor * max(1, len(specs)))()
+    for i, s in enumerate(specs):
+        for k, v in s.items():
+            setattr(arr[i], k, v)
+    return arr
+
+
+AGOOD = dict(param=0x10000000, grad=0x20000000, exp_avg=0x30000000, exp_avg_sq=0x40000000,
+             numel=1000, step=1, grad_dtype=muon.MUON_F32)
+
+
+def _acall(lib, arr, n, *, lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.01, ws=1 << 40, ws_bytes=1 << 30):
+    return lib.muon_adamw_step(arr, n, lr, b1, b2, eps, wd, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_adamw_argument_errors_are_caught_on_the_host(lib):
+    ok = _adam([AGOOD])
+    assert lib.muon_adamw_workspace_bytes(0) == 0 and lib.muon_adamw_workspace_bytes(3) > 0
+    assert _acall(lib, ok, 1, b1=1.0) == muon.MUON_EINVAL
+    assert _acall(lib, ok, 1, b2=-0.1) == muon.MUON_EINVAL
+    assert _acall(lib, ok, 1, eps=-1.0) == muon.MUON_EINVAL
+    assert _acall(lib, ok, 1, lr=float("inf")) == muon.MUON_EINVAL
+    assert _acall(lib, ok, -1) == muon.MUON_EINVAL
+    assert _acall(lib, _adam([dict(AGOOD, numel=0)]), 1) == muon.MUON_EINVAL
+    assert _acall(lib, _adam([dict(AGOOD, step=0)]), 1) == muon.MUON_EINVAL
+    assert _acall(lib, _adam([dict(AGOOD, reserved=1)]), 1) == muon.MUON_EINVAL
+    assert _acall(lib, _adam([dict(AGOOD, exp_avg=0)]), 1) == muon.MUON_EINVAL
+    assert _acall(lib, _adam([dict(AGOOD, grad_dtype=3)]), 1) == muon.MUON_EINVAL
+    assert _acall(lib, _adam([dict(AGOOD, param=0x10000002)]), 1) == muon.MUON_EINVAL
+    # second moment overlapping the param; two tensors sharing a first moment
+    assert _acall(lib, _adam([dict(AGOOD, exp_avg_sq=AGOOD["param"] + 400)]), 1) == muon.MUON_EALIAS
+    two = _adam([AGOOD, dict(AGOOD, param=0x50000000, grad=0x60000000, exp_avg_sq=0x70000000)])
+    assert _acall(lib, two, 2) == muon.MUON_EALIAS
+    need = lib.muon_adamw_workspace_bytes(1)
+    assert _acall(lib, ok, 1, ws_bytes=need - 1) == muon.MUON_EWORKSPACE
+    assert _acall(lib, ok, 1, ws=(1 << 40) + 8, ws_bytes=need) == muon.MUON_EWORKSPACE
+    # no gradients: validated, nothing launched
+    assert _acall(lib, _adam([dict(AGOOD, grad=0, step=0)]), 1) == muon.MUON_OK
+    assert _acall(lib, ok, 0) == muon.MUON_OK
