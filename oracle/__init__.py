@@ -5,6 +5,7 @@ from .muon_oracle import *  # noqa: F401,F403
 from .muon_oracle import (QUINTIC, CUBIC, HYBRID_TAIL, DEFAULT_EPS,  # noqa: F401
                           momentum_lerp, frobenius_norm, normalise,
                           needs_transpose, ns_iteration, newton_schulz,
-                          rms_scale, apply_update, muon_step_matrix, muon_step)
+                          rms_scale, apply_update, muon_step_matrix, muon_step,
+                          zero_center, nesterov_input)
 from .adamw_oracle import (ADAMW_LR, ADAMW_BETAS, ADAMW_EPS, ADAMW_WD,  # noqa: F401
                            adamw_step_tensor, adamw_step)

@@ -159,25 +159,62 @@ def apply_update(p, o, lr, wd, scale):
     return as_f64(p) * (1.0 - lr * wd) - lr * scale * as_f64(o)
 
 
+def zero_center(g):
+    """Subtract each column's mean: g - g.mean(dim=0, keepdim=True), the
+    ``zerocenter`` helper of [wmrh] section 2.1 (applied by ``_step_muon`` in
+    section 4.2 before the momentum).  Taken on the stored rows x cols
+    gradient, before any transpose to the short side."""
+    g = as_f64(g)
+    return g - g.mean(axis=0, keepdims=True)
+
+
+def nesterov_input(m_new, g, mu):
+    """NS input of the look-ahead variant.  The pages carry a ``nesterov``
+    flag but never define what it does ([wmrh] 4.1 accepts and ignores it;
+    [airosetta] selects the buffer).  The reading taken for the variant: the
+    iteration runs on mu * M_t + (1 - mu) * G_t, the gradient pulled toward
+    the new momentum (with M_t itself the EMA of the gradients)."""
+    return mu * as_f64(m_new) + (1.0 - mu) * as_f64(g)
+
+
 def muon_step_matrix(p, g, m, *, lr=0.02, mu=0.95, wd=0.0, ns_steps=5,
-                     coeffs=(QUINTIC,), eps=DEFAULT_EPS, rms_mode=None):
+                     coeffs=(QUINTIC,), eps=DEFAULT_EPS, rms_mode=None,
+                     zero_centering=False, nesterov=False, ns_first=False):
     """One Muon step on one 2-D parameter, in the pages' order
     (momentum, then orthogonalisation, then decayed update; [wmrh] 4.2 picks
     momentum before Newton-Schulz, as does [airosetta]).
 
+    Variants ([wmrh] sections 2.1 and 4.2):
+    ``zero_centering`` subtracts the gradient's column means first;
+    ``ns_first`` takes the other order the page discusses, zero-center ->
+    Newton-Schulz -> momentum buffer -> update: the momentum averages the
+    orthogonalised gradients and the update is -lr * s * M;
+    ``nesterov`` runs the iteration on ``nesterov_input`` (not with
+    ``ns_first``: the pages give that combination no meaning).
+
     Returns a dict with every stage so each can be compared on its own:
-    ``m`` (new momentum), ``nu`` (||M||_F), ``o`` (orthogonalised update),
-    ``p`` (new parameter), ``scale`` (the RMS scale used).
-    When ``g`` is None the matrix is skipped ([airosetta] Muon.step skips
-    parameters without a gradient): nothing changes.
+    ``m`` (new momentum), ``nu`` (Frobenius norm of the NS input), ``o``
+    (orthogonalised matrix), ``p`` (new parameter), ``scale`` (the RMS scale
+    used).  When ``g`` is None the matrix is skipped ([airosetta] Muon.step
+    skips parameters without a gradient): nothing changes.
     """
     if g is None:
         return {"m": as_f64(m), "nu": None, "o": None, "p": as_f64(p), "scale": None}
+    if nesterov and ns_first:
+        raise ValueError("nesterov and ns_first together are not defined")
     rows, cols = np.shape(g)
-    m_new = momentum_lerp(m, g, mu)
-    nu = frobenius_norm(m_new)
-    o = newton_schulz(m_new, coeffs, ns_steps, eps)
+    g = zero_center(g) if zero_centering else as_f64(g)
     s = rms_scale(rows, cols, rms_mode)
+    if ns_first:
+        nu = frobenius_norm(g)
+        o = newton_schulz(g, coeffs, ns_steps, eps)
+        m_new = momentum_lerp(m, o, mu)
+        p_new = apply_update(p, m_new, lr, wd, s)
+        return {"m": m_new, "nu": nu, "o": o, "p": p_new, "scale": s}
+    m_new = momentum_lerp(m, g, mu)
+    x = nesterov_input(m_new, g, mu) if nesterov else m_new
+    nu = frobenius_norm(x)
+    o = newton_schulz(x, coeffs, ns_steps, eps)
     p_new = apply_update(p, o, lr, wd, s)
     return {"m": m_new, "nu": nu, "o": o, "p": p_new, "scale": s}
 
