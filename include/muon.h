@@ -130,6 +130,40 @@ int muon_step(const muon_matrix_t* mats, int64_t n_mats,
               int rms_scale_mode, float eps,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Step variants, as flags of muon_options_t (any combination except
+ * NESTEROV | NS_FIRST).
+ *   MUON_OPT_ZERO_CENTER  G <- G minus its column means (the mean over rows of
+ *       each column of the stored rows x cols gradient), before anything else
+ *       uses G ("Muon meets Mamba", wmrh.cn, section 2.1 zerocenter, applied by
+ *       _step_muon in section 4.2).  Costs one extra read of G (a column-sum
+ *       pass with fp64 accumulation) and sizeof(double) * cols of workspace,
+ *       which muon_workspace_bytes() always reserves.
+ *   MUON_OPT_NESTEROV     the iteration runs on mu*M_new + (1-mu)*G instead
+ *       of M_new.  The pages carry a nesterov switch but never say what it
+ *       computes (airosetta.com, Muon constructor; wmrh.cn section 4.1); this
+ *       look-ahead form is the reading taken.  M itself is still the EMA.
+ *   MUON_OPT_NS_FIRST     the other order that wmrh.cn section 4.2 discusses:
+ *       O = NS(G / (||G||_F + eps)), then M <- mu*M + (1-mu)*O and
+ *       p <- p*(1 - lr*wd) - lr*s*M.  The norm slot of the workspace then
+ *       holds ||G||_F^2. */
+#define MUON_OPT_ZERO_CENTER 1u
+#define MUON_OPT_NESTEROV    2u
+#define MUON_OPT_NS_FIRST    4u
+typedef struct {
+  uint32_t flags;     /* MUON_OPT_* */
+  uint32_t reserved;  /* must be 0 */
+} muon_options_t;
+
+/* muon_step with step variants.  options == NULL (or flags == 0) is exactly
+ * muon_step.  Unknown flags, reserved != 0 or NESTEROV together with
+ * NS_FIRST give MUON_EINVAL before anything is launched; everything else is
+ * as muon_step. */
+int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats,
+                 float lr, float mu, float wd, int ns_steps,
+                 const muon_ns_coeff_t* coeffs, int n_coeffs,
+                 int rms_scale_mode, float eps, const muon_options_t* options,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Orthogonalisation alone: out = NS(in) with the same normalisation,
  * short-side rule and bf16 iteration as muon_step, for a list of matrices.
  * The Newton-Schulz routine of the airosetta.com article (newtonschulz5) as a

@@ -15,7 +15,8 @@ from typing import Iterable, Sequence
 
 from . import _lib
 from ._lib import (MUON_BF16, MUON_EALIAS, MUON_EHIP, MUON_EINVAL, MUON_EWORKSPACE,  # noqa: F401
-                   MUON_F32, MUON_OK, MUON_SCALE_NONE, MUON_SCALE_SQRT_MAX1, PHASE_NAMES,
+                   MUON_F32, MUON_OK, MUON_OPT_NESTEROV, MUON_OPT_NS_FIRST, MUON_OPT_ZERO_CENTER,
+                   MuonOptions, MUON_SCALE_NONE, MUON_SCALE_SQRT_MAX1, PHASE_NAMES,
                    LibMuonError, MuonAdamWTensor, MuonCoeff, MuonMatrix, MuonOrtho,
                    MuonWorkspaceView, status_string)
 
@@ -118,11 +119,13 @@ def _stream_handle(stream, device):
 def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 0.02,
               mu: float = 0.95, wd: float = 0.0, ns_steps: int = 5, coeffs=QUINTIC,
               rms_scale: str | None = None, eps: float = 1e-7, scales: Sequence | None = None,
+              zero_centering: bool = False, nesterov: bool = False, ns_first: bool = False,
               workspace=None, stream=None):
     """One Muon step over lists of 2-D fp32 params, grads (fp32 or bf16, or
     None to skip) and fp32 momentum buffers, all on one GPU.  Updates params
     and momenta in place on ``stream`` (default: the current stream) and
-    returns the workspace tensor used."""
+    returns the workspace tensor used.  ``zero_centering``, ``nesterov`` and
+    ``ns_first`` select the step variants of ``muon_step_ex``."""
     torch = _torch()
     n = len(params)
     if len(grads) != n or len(moms) != n:
@@ -150,10 +153,18 @@ def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 
     if workspace is None:
         workspace = alloc_workspace([tuple(p.shape) for p in params], device)
     carr, nc = _coeff_array(coeffs, ns_steps)
-    st = _lib.load().muon_step(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
-                               mode, float(eps), ctypes.c_void_p(workspace.data_ptr()),
-                               workspace.numel() * workspace.element_size(),
-                               _stream_handle(stream, device))
+    flags = ((MUON_OPT_ZERO_CENTER if zero_centering else 0) | (MUON_OPT_NESTEROV if nesterov else 0)
+             | (MUON_OPT_NS_FIRST if ns_first else 0))
+    lib = _lib.load()
+    ws_args = (ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+               _stream_handle(stream, device))
+    if flags:
+        opts = MuonOptions(flags, 0)
+        st = lib.muon_step_ex(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
+                              mode, float(eps), ctypes.byref(opts), *ws_args)
+    else:
+        st = lib.muon_step(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
+                           mode, float(eps), *ws_args)
     _lib.check(st, "muon_step")
     return workspace
 

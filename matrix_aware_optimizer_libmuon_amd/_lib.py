@@ -24,11 +24,16 @@ MUON_BF16 = 1
 MUON_SCALE_NONE = 0
 MUON_SCALE_SQRT_MAX1 = 1
 
+MUON_OPT_ZERO_CENTER = 1
+MUON_OPT_NESTEROV = 2
+MUON_OPT_NS_FIRST = 4
+
 MUON_PHASES = 7
 PHASE_NAMES = ("momentum_norm", "normalize_cast", "gram", "gram2_epilogue", "x_update", "apply",
                "adamw")
 
-EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_orthogonalize", "muon_workspace_view",
+EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_step_ex", "muon_orthogonalize",
+            "muon_workspace_view",
             "muon_adamw_workspace_bytes", "muon_adamw_step",
             "muon_timing_enable", "muon_timing_read", "muon_status_string", "muon_version")
 
@@ -38,6 +43,10 @@ class MuonMatrix(ctypes.Structure):
                 ("momentum", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("grad_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float)]
+
+
+class MuonOptions(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class MuonOrtho(ctypes.Structure):
@@ -89,6 +98,11 @@ def load() -> ctypes.CDLL:
                               ctypes.c_float, ctypes.c_int, P(MuonCoeff), ctypes.c_int, ctypes.c_int,
                               ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.muon_step.restype = ctypes.c_int
+    lib.muon_step_ex.argtypes = [P(MuonMatrix), ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_int, P(MuonCoeff), ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_float, P(MuonOptions), ctypes.c_void_p,
+                                 ctypes.c_size_t, ctypes.c_void_p]
+    lib.muon_step_ex.restype = ctypes.c_int
     lib.muon_orthogonalize.argtypes = [P(MuonOrtho), ctypes.c_int64, ctypes.c_int, P(MuonCoeff),
                                        ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]

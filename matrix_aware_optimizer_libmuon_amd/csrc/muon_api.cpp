@@ -29,15 +29,17 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 // workspace plan (a pure function of the shapes)
 //
-//   [ table: MatDesc[n] | 7 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
+//   [ table: MatDesc[n] | 8 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
+//   [ column sums: double[cols] per matrix ] (256-aligned; zero-centering only)
 //   then, per matrix (all n, skipped ones included):
 //   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | C ] m_pad x m_pad bf16 each,
 //   and [ C_lo ] m_pad x m_pad bf16 when the short side is <= kSplitMaxM
 // ---------------------------------------------------------------------------
 // prefix arrays of the table: element chunks (flat / padded) over all active
-// matrices, then symmetric and full tile counts per tile class
+// matrices, symmetric and full tile counts per tile class, row groups of the
+// apply pass, and column-sum blocks (zero-centering matrices only)
 enum { kPreFlat = 0, kPrePad = 1, kPreSymBig = 2, kPreFullBig = 3, kPreSymSmall = 4,
-       kPreFullSmall = 5, kPreRows = 6, kNumPrefix = 7 };
+       kPreFullSmall = 5, kPreRows = 6, kPreCol = 7, kNumPrefix = 8 };
 
 int tile_class(int64_t r, int64_t c) { return std::min(r, c) >= kBigMinM ? kTileBig : kTileSmall; }
 
@@ -45,12 +47,14 @@ struct MatPlan {
   int64_t rows, cols, rows_pad, cols_pad, m_pad, n_pad;
   int tile;
   bool tall, split;
-  size_t x_off[2], a_off, b_off, blo_off;
+  size_t x_off[2], a_off, b_off, blo_off, colsum_off;
 };
 
 struct Plan {
   int64_t n = 0;
   size_t desc_off = 0, prefix_off[kNumPrefix] = {}, nrm2_off = 0, table_bytes = 0;
+  size_t colsum_off = 0;
+  int64_t colsum_count = 0;           // doubles in the column-sum region
   size_t total = 0;
   std::vector<MatPlan> mats;
 };
@@ -70,8 +74,8 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
   plan.nrm2_off = off;
   off += static_cast<size_t>(n) * sizeof(double);
   plan.table_bytes = align_up(off, kAlign);
-  off = plan.table_bytes;
   plan.mats.resize(static_cast<size_t>(n));
+  plan.colsum_off = plan.table_bytes;
   for (int64_t i = 0; i < n; ++i) {
     int64_t r, c;
     shape(i, r, c);
@@ -79,6 +83,13 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
     MatPlan& m = plan.mats[static_cast<size_t>(i)];
     m.rows = r;
     m.cols = c;
+    m.colsum_off = plan.colsum_off + static_cast<size_t>(plan.colsum_count) * sizeof(double);
+    plan.colsum_count += c;
+  }
+  off = align_up(plan.colsum_off + static_cast<size_t>(plan.colsum_count) * sizeof(double), kAlign);
+  for (int64_t i = 0; i < n; ++i) {
+    MatPlan& m = plan.mats[static_cast<size_t>(i)];
+    const int64_t r = m.rows, c = m.cols;
     m.tile = tile_class(r, c);
     m.rows_pad = round_up(r, m.tile);
     m.cols_pad = round_up(c, m.tile);
@@ -286,6 +297,8 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
       // row groups of about kChunk elements for the normalise / apply passes
       d.rg_pad = static_cast<int32_t>(std::max<int64_t>(1, kChunk / m.cols_pad));
       d.rg = static_cast<int32_t>(std::max<int64_t>(1, kChunk / m.cols));
+      d.colsum = reinterpret_cast<double*>(ws + m.colsum_off);
+      d.inv_rows = 1.0 / static_cast<double>(m.rows);
       desc[a] = d;
       const int64_t flat = m.rows * m.cols;
       const int64_t t_side = m.m_pad / m.tile;
@@ -295,6 +308,9 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
       acc[kPrePad] += (m.rows_pad + d.rg_pad - 1) / d.rg_pad;
       pre[kPreRows][a] = acc[kPreRows];
       acc[kPreRows] += (m.rows + d.rg - 1) / d.rg;
+      pre[kPreCol][a] = acc[kPreCol];
+      if (d.flags & kFlagZeroCenter)
+        acc[kPreCol] += ((m.rows + kColRows - 1) / kColRows) * ((m.cols + kColCols - 1) / kColCols);
       pre[sym][local] = acc[sym];
       acc[sym] += t_side * (t_side + 1) / 2;
       pre[full][local] = acc[full];
@@ -309,6 +325,7 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
   pre[kPreFlat][a] = acc[kPreFlat];
   pre[kPrePad][a] = acc[kPrePad];
   pre[kPreRows][a] = acc[kPreRows];
+  pre[kPreCol][a] = acc[kPreCol];
   for (int k = 0; k < kNumPrefix; ++k) t.units[k] = acc[k];
 }
 
@@ -324,12 +341,20 @@ int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float l
   const int n = t.n_active, nb = t.n_big, ns = n - nb;
   const MatDesc* d_small = d + nb;
   void* s = static_cast<void*>(stream);
+  if (t.units[kPreCol] > 0) {
+    // zero-centering: column sums of G first (counted with the momentum phase)
+    rc = timed(kPhaseMomentumNorm, stream, [&] {
+      return launch_colsum(d, pre[kPreCol], n, t.units[kPreCol],
+                           reinterpret_cast<double*>(ws + plan.colsum_off), plan.colsum_count, s);
+    });
+    if (rc) return rc;
+  }
   rc = timed(kPhaseMomentumNorm, stream, [&] {
     return launch_momentum_norm(d, pre[kPreFlat], n, t.units[kPreFlat], mu, ortho ? 1 : 0, s);
   });
   if (rc) return rc;
   rc = timed(kPhaseNormalize, stream, [&] {
-    return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, s);
+    return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, mu, s);
   });
   if (rc) return rc;
   for (int k = 0; k < ns_steps; ++k) {
@@ -358,7 +383,7 @@ int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float l
     if (rc) return rc;
   }
   rc = timed(kPhaseApply, stream, [&] {
-    return launch_apply(d, pre[kPreRows], n, t.units[kPreRows], ns_steps & 1, lr, wd, ortho ? 1 : 0, s);
+    return launch_apply(d, pre[kPreRows], n, t.units[kPreRows], ns_steps & 1, lr, wd, mu, ortho ? 1 : 0, s);
   });
   return rc;
 }
@@ -375,9 +400,19 @@ size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n_mats) {
   return plan.total;
 }
 
-int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd, int ns_steps,
-              const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
-              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd,
+                 int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode,
+                 float eps, const muon_options_t* options, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  uint32_t variant = 0;
+  if (options) {
+    const uint32_t known = MUON_OPT_ZERO_CENTER | MUON_OPT_NESTEROV | MUON_OPT_NS_FIRST;
+    if ((options->flags & ~known) != 0 || options->reserved != 0) return MUON_EINVAL;
+    if ((options->flags & MUON_OPT_NESTEROV) && (options->flags & MUON_OPT_NS_FIRST)) return MUON_EINVAL;
+    if (options->flags & MUON_OPT_ZERO_CENTER) variant |= kFlagZeroCenter;
+    if (options->flags & MUON_OPT_NESTEROV) variant |= kFlagNesterov;
+    if (options->flags & MUON_OPT_NS_FIRST) variant |= kFlagNsFirst;
+  }
   if (n_mats < 0 || (n_mats > 0 && !mats)) return MUON_EINVAL;
   if (n_mats > (int64_t(1) << 24)) return MUON_EINVAL;
   if (!finite(lr) || !finite(mu) || !finite(wd)) return MUON_EINVAL;
@@ -417,6 +452,7 @@ int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, flo
     d.param = m.param;
     d.grad = m.grad;
     d.mom = m.momentum;
+    d.flags |= variant;
     const bool bf = m.grad_dtype == MUON_BF16;
     if (bf) d.flags |= kFlagGradBf16;
     const int64_t el = m.rows * m.cols;
@@ -430,6 +466,13 @@ int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, flo
     return true;
   }, t);
   return run_sequence(plan, t, ws, false, lr, mu, wd, ns_steps, coeffs, n_coeffs, eps, stream);
+}
+
+int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd, int ns_steps,
+              const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return muon_step_ex(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs, rms_scale_mode, eps,
+                      nullptr, workspace, workspace_bytes, stream);
 }
 
 int muon_orthogonalize(const muon_ortho_t* mats, int64_t n_mats, int ns_steps,

@@ -42,6 +42,10 @@ enum : uint32_t {
   kFlagVecFlat = 4u,     // param/grad/mom 16-byte aligned and rows*cols % 8 == 0
   kFlagVecRows = 8u,     // additionally cols % 8 == 0 (row-wise 8-vectors)
   kFlagSplitC = 16u,     // C kept as a bf16 hi + lo pair (short side <= kSplitMaxM)
+  // step variants (muon_step_ex options)
+  kFlagZeroCenter = 32u, // G <- G - column means (colsum / rows) before use
+  kFlagNesterov = 64u,   // NS input mu M_new + (1 - mu) G
+  kFlagNsFirst = 128u,   // NS on G, then M <- mu M + (1 - mu) O and the update uses M
 };
 
 // Matrices whose short side is at most this keep C = a I + b A + c A A as a
@@ -50,7 +54,7 @@ enum : uint32_t {
 // pass is one 128-wide tile row, i.e. negligible work.
 constexpr int kSplitMaxM = 128;
 
-// One matrix, as the kernels see it.  128 bytes.
+// One matrix, as the kernels see it.  144 bytes.
 struct alignas(16) MatDesc {
   float* param;          // fp32 rows x cols (muon_step) / unused (orthogonalize)
   const void* grad;      // grad (muon_step) or input (orthogonalize)
@@ -67,8 +71,15 @@ struct alignas(16) MatDesc {
   float scale;           // update scale s
   int32_t rg_pad;        // rows per work unit of the normalise pass (over rows_pad)
   int32_t rg;            // rows per work unit of the apply pass (over rows)
+  double* colsum;        // column sums of G (kFlagZeroCenter), cols doubles
+  double inv_rows;       // 1 / rows
 };
-static_assert(sizeof(MatDesc) == 128, "descriptor size");
+static_assert(sizeof(MatDesc) == 144, "descriptor size");
+
+// Column-sum pass of zero-centering: one work unit = kColRows rows x
+// kColCols columns of one matrix.
+constexpr int kColRows = 256;
+constexpr int kColCols = 2048;
 
 // One AdamW tensor, as the kernel sees it.  64 bytes.  The per-tensor bias
 // corrections are folded on the host: step_size = lr / (1 - beta1^t),
@@ -89,7 +100,9 @@ static_assert(sizeof(AdamDesc) == 64, "AdamW descriptor size");
 int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                          float mu, int norm_only, void* stream);
 int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
-                     float eps, void* stream);
+                     float eps, float mu, void* stream);
+int launch_colsum(const MatDesc* d, const int64_t* prefix, int n, int64_t units, double* zero_from,
+                  int64_t zero_count, void* stream);
 // GEMM phases: `tile` is 128 or 256; every matrix of the launch is of that class
 int launch_gram(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                 int parity, void* stream);
@@ -98,7 +111,7 @@ int launch_gram2(int tile, const MatDesc* d, const int64_t* prefix, int n, int64
 int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                    int parity, void* stream);
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                 float lr, float wd, int export_only, void* stream);
+                 float lr, float wd, float mu, int export_only, void* stream);
 int launch_adamw(const AdamDesc* d, const int64_t* prefix, int n, int64_t units, float beta1,
                  float beta2, float eps, void* stream);
 

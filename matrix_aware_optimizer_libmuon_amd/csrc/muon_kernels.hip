@@ -24,7 +24,12 @@
 namespace muon {
 
 // ---------------------------------------------------------------------------
-// K1: M <- mu M + (1 - mu) G, and sum of M^2 (norm_only: sum of G^2, no update)
+// K1: M <- mu M + (1 - mu) G, and the sum of squares of the NS input:
+//   default          sum of M^2
+//   kFlagNesterov    sum of (mu M + (1 - mu) G)^2
+//   kFlagNsFirst /   sum of G^2, no momentum update (the momentum comes after
+//   norm_only        the iteration, or there is none: orthogonalize)
+// With kFlagZeroCenter, G is first replaced by G - colsum / rows.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void load8_src(const void* src, bool bf16, int64_t e, float (&v)[8]) {
   if (bf16) {
@@ -50,6 +55,35 @@ __device__ __forceinline__ float load1_src(const void* src, bool bf16, int64_t e
               : gld<float>(static_cast<const float*>(src) + e);
 }
 
+// Column index of a flat element index, advanced by a fixed stride without
+// a division per step.
+struct ColWalk {
+  int64_t c, sc, w;
+  __device__ ColWalk(int64_t first, int64_t stride, int64_t width)
+      : c(first % width), sc(stride % width), w(width) {}
+  __device__ void next() {
+    c += sc;
+    if (c >= w) c -= w;
+  }
+};
+
+// g[j] -= mean of column c + j, j < K.  The mean is formed in fp64 and
+// rounded once, so a column of equal values centres to exact zeros.
+template <int K>
+__device__ __forceinline__ void center(float (&g)[K], const MatDesc& d, int64_t c) {
+#pragma unroll
+  for (int j = 0; j < K; ++j) g[j] -= static_cast<float>(gld<double>(d.colsum + c + j) * d.inv_rows);
+}
+
+// one element of K1; returns its contribution to the sum of squares
+__device__ __forceinline__ float k1_elem(float& m, float g, float mu, float omu, bool update,
+                                         bool nest) {
+  if (!update) return g * g;
+  m = fmaf(mu, m, omu * g);
+  const float x = nest ? fmaf(mu, m, omu * g) : m;
+  return x * x;
+}
+
 __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n,
     float mu, float omu, int norm_only) {
@@ -61,16 +95,27 @@ __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
   const int64_t begin = (unit - prefix[i]) * kChunk;
   const int64_t end = begin + kChunk < total ? begin + kChunk : total;
   const bool gbf = (d.flags & kFlagGradBf16) != 0;
+  const bool zc = (d.flags & kFlagZeroCenter) != 0;
+  const bool nest = (d.flags & kFlagNesterov) != 0;
+  const bool update = !norm_only && !(d.flags & kFlagNsFirst);
   constexpr int S = kEwThreads * 8;  // elements per block-wide vector step
   float acc = 0.f;
-  if (d.flags & kFlagVecFlat) {
+  // with zero-centering the 8-vector must stay in one row: cols % 8 == 0
+  if ((d.flags & kFlagVecFlat) && (!zc || (d.flags & kFlagVecRows))) {
     int64_t e = begin + threadIdx.x * 8;
+    ColWalk cw(zc ? e : 0, S, zc ? d.cols : 1);
     // two 8-element vectors in flight per thread
     for (; e + S < end; e += 2 * S) {
       float g0[8], g1[8];
       load8_src(d.grad, gbf, e, g0);
       load8_src(d.grad, gbf, e + S, g1);
-      if (norm_only) {
+      if (zc) {
+        center<8>(g0, d, cw.c);
+        cw.next();
+        center<8>(g1, d, cw.c);
+        cw.next();
+      }
+      if (!update) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc = fmaf(g0[j], g0[j], fmaf(g1[j], g1[j], acc));
       } else {
@@ -78,14 +123,12 @@ __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
         f32x4 m2 = gld<f32x4>(d.mom + e + S), m3 = gld<f32x4>(d.mom + e + S + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          m0[j] = fmaf(mu, m0[j], omu * g0[j]);
-          m1[j] = fmaf(mu, m1[j], omu * g0[4 + j]);
-          m2[j] = fmaf(mu, m2[j], omu * g1[j]);
-          m3[j] = fmaf(mu, m3[j], omu * g1[4 + j]);
-          acc = fmaf(m0[j], m0[j], acc);
-          acc = fmaf(m1[j], m1[j], acc);
-          acc = fmaf(m2[j], m2[j], acc);
-          acc = fmaf(m3[j], m3[j], acc);
+          float a = m0[j], b = m1[j], c = m2[j], q = m3[j];
+          acc += k1_elem(a, g0[j], mu, omu, true, nest);
+          acc += k1_elem(b, g0[4 + j], mu, omu, true, nest);
+          acc += k1_elem(c, g1[j], mu, omu, true, nest);
+          acc += k1_elem(q, g1[4 + j], mu, omu, true, nest);
+          m0[j] = a, m1[j] = b, m2[j] = c, m3[j] = q;
         }
         gst<f32x4>(d.mom + e, m0);
         gst<f32x4>(d.mom + e + 4, m1);
@@ -96,36 +139,83 @@ __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
     if (e < end) {
       float g[8];
       load8_src(d.grad, gbf, e, g);
-      if (norm_only) {
+      if (zc) center<8>(g, d, cw.c);
+      if (!update) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc = fmaf(g[j], g[j], acc);
       } else {
         f32x4 m0 = gld<f32x4>(d.mom + e), m1 = gld<f32x4>(d.mom + e + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          m0[j] = fmaf(mu, m0[j], omu * g[j]);
-          m1[j] = fmaf(mu, m1[j], omu * g[4 + j]);
-          acc = fmaf(m0[j], m0[j], acc);
-          acc = fmaf(m1[j], m1[j], acc);
+          float a = m0[j], b = m1[j];
+          acc += k1_elem(a, g[j], mu, omu, true, nest);
+          acc += k1_elem(b, g[4 + j], mu, omu, true, nest);
+          m0[j] = a, m1[j] = b;
         }
         gst<f32x4>(d.mom + e, m0);
         gst<f32x4>(d.mom + e + 4, m1);
       }
     }
   } else {
-    for (int64_t e = begin + threadIdx.x; e < end; e += kEwThreads) {
-      const float g = load1_src(d.grad, gbf, e);
-      if (norm_only) {
-        acc = fmaf(g, g, acc);
+    int64_t e = begin + threadIdx.x;
+    ColWalk cw(zc ? e : 0, kEwThreads, zc ? d.cols : 1);
+    for (; e < end; e += kEwThreads, cw.next()) {
+      float g[1] = {load1_src(d.grad, gbf, e)};
+      if (zc) center<1>(g, d, cw.c);
+      if (!update) {
+        acc = fmaf(g[0], g[0], acc);
       } else {
-        const float m = fmaf(mu, gld<float>(d.mom + e), omu * g);
+        float m = gld<float>(d.mom + e);
+        acc += k1_elem(m, g[0], mu, omu, true, nest);
         gst<float>(d.mom + e, m);
-        acc = fmaf(m, m, acc);
       }
     }
   }
   const double s = block_sum_256(static_cast<double>(acc), red);
   if (threadIdx.x == 0) unsafeAtomicAdd(d.nrm2, s);
+}
+
+// ---------------------------------------------------------------------------
+// Zero-centering, first pass: column sums of G into colsum (fp64 sums and
+// atomics).
+// Block 0 of the launch is preceded by a fill kernel zeroing every colsum.
+// One work unit = kColRows rows x kColCols columns; a thread owns 8 columns.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kEwThreads) void k_fill_zero_f64(double* p, int64_t count) {
+  for (int64_t k = blockIdx.x * static_cast<int64_t>(kEwThreads) + threadIdx.x; k < count;
+       k += static_cast<int64_t>(gridDim.x) * kEwThreads)
+    p[k] = 0.0;
+}
+
+__global__ __launch_bounds__(kEwThreads) void k_colsum(const MatDesc* __restrict__ descs,
+                                                       const int64_t* __restrict__ prefix, int n) {
+  const int64_t unit = blockIdx.x;
+  const int i = find_matrix(prefix, n, unit);
+  const MatDesc& d = descs[i];
+  const int64_t ncc = (d.cols + kColCols - 1) / kColCols;
+  const int64_t u = unit - prefix[i];
+  const int64_t r0 = (u / ncc) * kColRows, c0 = (u % ncc) * kColCols;
+  const int64_t r1 = r0 + kColRows < d.rows ? r0 + kColRows : d.rows;
+  const bool gbf = (d.flags & kFlagGradBf16) != 0;
+  if (d.flags & kFlagVecRows) {  // cols % 8 == 0 and 16-byte aligned rows
+    const int64_t c = c0 + threadIdx.x * 8;
+    if (c >= d.cols) return;
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int64_t r = r0; r < r1; ++r) {
+      float g[8];
+      load8_src(d.grad, gbf, r * d.cols + c, g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += static_cast<double>(g[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) unsafeAtomicAdd(d.colsum + c + j, acc[j]);
+  } else {
+    for (int64_t c = c0 + threadIdx.x; c < c0 + kColCols && c < d.cols; c += kEwThreads) {
+      double acc = 0.0;
+      for (int64_t r = r0; r < r1; ++r) acc += static_cast<double>(load1_src(d.grad, gbf, r * d.cols + c));
+      unsafeAtomicAdd(d.colsum + c, acc);
+    }
+  }
 }
 
 // Walks a row-major block of rows [r0, r1) x [0, w) in steps of `step`
@@ -150,17 +240,22 @@ struct RowWalk {
 };
 
 // ---------------------------------------------------------------------------
-// K2: X0 = bf16(M / (||M|| + eps)) into the zero-padded rows_pad x cols_pad buffer.
-// One work unit = rg_pad padded rows.
+// K2: X0 = bf16(N / (||N|| + eps)) into the zero-padded rows_pad x cols_pad
+// buffer, N the NS input: M (default), the input (orthogonalize), G
+// (kFlagNsFirst; centered with kFlagZeroCenter) or mu M + (1 - mu) G
+// (kFlagNesterov).  One work unit = rg_pad padded rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kEwThreads) void k_normalize(
-    const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, float eps) {
+    const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, float eps,
+    float mu) {
   const int64_t unit = blockIdx.x;
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
-  const bool ortho = d.mom == nullptr;  // orthogonalize: the source is the input
-  const void* src = ortho ? d.grad : static_cast<const void*>(d.mom);
-  const bool sbf = ortho && (d.flags & kFlagGradBf16);
+  const bool from_grad = d.mom == nullptr || (d.flags & kFlagNsFirst);  // N = G
+  const bool nest = (d.flags & kFlagNesterov) != 0;                    // N = mu M + (1-mu) G
+  const bool zc = (d.flags & kFlagZeroCenter) != 0;
+  const bool gbf = (d.flags & kFlagGradBf16) != 0;
+  const float omu = 1.0f - mu;
   const float inv = static_cast<float>(1.0 / (sqrt(gld<double>(d.nrm2)) + static_cast<double>(eps)));
   const int cp = d.cols_pad;
   const int64_t r0 = (unit - prefix[i]) * d.rg_pad;
@@ -174,11 +269,36 @@ __global__ __launch_bounds__(kEwThreads) void k_normalize(
     const int64_t r = p.r, c0 = p.c;
     float v[8];
     if (r < d.rows && vec && c0 + 8 <= d.cols) {
-      load8_src(src, sbf, r * d.cols + c0, v);
+      const int64_t g = r * d.cols + c0;
+      if (from_grad || nest) {
+        load8_src(d.grad, gbf, g, v);
+        if (zc) center<8>(v, d, c0);
+      }
+      if (nest) {
+        const f32x4 m0 = gld<f32x4>(d.mom + g), m1 = gld<f32x4>(d.mom + g + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = fmaf(mu, m0[j], omu * v[j]);
+          v[4 + j] = fmaf(mu, m1[j], omu * v[4 + j]);
+        }
+      } else if (!from_grad) {
+        load8_src(d.mom, false, g, v);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = (r < d.rows && c0 + j < d.cols) ? load1_src(src, sbf, r * d.cols + c0 + j) : 0.f;
+      for (int j = 0; j < 8; ++j) {
+        v[j] = 0.f;
+        if (r < d.rows && c0 + j < d.cols) {
+          const int64_t g = r * d.cols + c0 + j;
+          float gv[1] = {0.f};
+          if (from_grad || nest) {
+            gv[0] = load1_src(d.grad, gbf, g);
+            if (zc) center<1>(gv, d, c0 + j);
+          }
+          v[j] = nest ? fmaf(mu, gld<float>(d.mom + g), omu * gv[0])
+                      : (from_grad ? gv[0] : gld<float>(d.mom + g));
+        }
+      }
     }
     u32x4 o;
 #pragma unroll
@@ -188,12 +308,13 @@ __global__ __launch_bounds__(kEwThreads) void k_normalize(
 }
 
 // ---------------------------------------------------------------------------
-// K5: p <- p (1 - lr wd) - lr s O    (export_only: out <- O, unpadded).
+// K5: p <- p (1 - lr wd) - lr s O    (export_only: out <- O, unpadded);
+// with kFlagNsFirst: M <- mu M + (1 - mu) O, then p <- p (1 - lr wd) - lr s M.
 // One work unit = rg rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kEwThreads) void k_apply(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, int parity,
-    float lr, float wd, int export_only) {
+    float lr, float wd, float mu, int export_only) {
   const int64_t unit = blockIdx.x;
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
@@ -205,6 +326,8 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
   const int64_t count = (r1 - r0) * cols;
   const float decay = 1.0f - lr * wd;
   const float step = lr * d.scale;
+  const bool after = !export_only && (d.flags & kFlagNsFirst);
+  const float omu = 1.0f - mu;
   if (d.flags & kFlagVecRows) {
     constexpr int S = kEwThreads * 8;
     RowWalk p(r0, threadIdx.x * 8, S, cols);
@@ -214,13 +337,29 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
       if (export_only) {
         gst<u32x4>(d.out + g, q);
       } else {
+        float u[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u[2 * j] = __uint_as_float(q[j] << 16);
+          u[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+        }
+        if (after) {
+          f32x4 m0 = gld<f32x4>(d.mom + g), m1 = gld<f32x4>(d.mom + g + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            m0[j] = fmaf(mu, m0[j], omu * u[j]);
+            m1[j] = fmaf(mu, m1[j], omu * u[4 + j]);
+            u[j] = m0[j];
+            u[4 + j] = m1[j];
+          }
+          gst<f32x4>(d.mom + g, m0);
+          gst<f32x4>(d.mom + g + 4, m1);
+        }
         f32x4 p0 = gld<f32x4>(d.param + g), p1 = gld<f32x4>(d.param + g + 4);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          p0[2 * j] = fmaf(-step, __uint_as_float(q[j] << 16), p0[2 * j] * decay);
-          p0[2 * j + 1] = fmaf(-step, __uint_as_float(q[j] & 0xffff0000u), p0[2 * j + 1] * decay);
-          p1[2 * j] = fmaf(-step, __uint_as_float(q[2 + j] << 16), p1[2 * j] * decay);
-          p1[2 * j + 1] = fmaf(-step, __uint_as_float(q[2 + j] & 0xffff0000u), p1[2 * j + 1] * decay);
+        for (int j = 0; j < 4; ++j) {
+          p0[j] = fmaf(-step, u[j], p0[j] * decay);
+          p1[j] = fmaf(-step, u[4 + j], p1[j] * decay);
         }
         gst<f32x4>(d.param + g, p0);
         gst<f32x4>(d.param + g + 4, p1);
@@ -231,8 +370,16 @@ __global__ __launch_bounds__(kEwThreads) void k_apply(
     for (int64_t e = threadIdx.x; e < count; e += kEwThreads, p.next()) {
       const int64_t r = p.r, c = p.c, g = r * cols + c;
       const uint16_t q = gld<uint16_t>(o + r * cp + c);
-      if (export_only) gst<uint16_t>(d.out + g, q);
-      else gst<float>(d.param + g, fmaf(-step, bf2f(q), gld<float>(d.param + g) * decay));
+      if (export_only) {
+        gst<uint16_t>(d.out + g, q);
+      } else {
+        float u = bf2f(q);
+        if (after) {
+          u = fmaf(mu, gld<float>(d.mom + g), omu * u);
+          gst<float>(d.mom + g, u);
+        }
+        gst<float>(d.param + g, fmaf(-step, u, gld<float>(d.param + g) * decay));
+      }
     }
   }
 }
@@ -310,10 +457,23 @@ int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t
 }
 
 int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float eps,
-                     void* stream) {
+                     float mu, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_normalize, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, eps);
+                     static_cast<hipStream_t>(stream), d, prefix, n, eps, mu);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_colsum(const MatDesc* d, const int64_t* prefix, int n, int64_t units, double* zero_from,
+                  int64_t zero_count, void* stream) {
+  if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t fill_blocks = (zero_count + kEwThreads - 1) / kEwThreads;
+  hipLaunchKernelGGL(k_fill_zero_f64, dim3(static_cast<unsigned>(fill_blocks < 1024 ? fill_blocks : 1024)),
+                     dim3(kEwThreads), 0, st, zero_from, zero_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return static_cast<int>(e);
+  hipLaunchKernelGGL(k_colsum, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0, st, d, prefix, n);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -339,10 +499,10 @@ int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int
 }
 
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                 float lr, float wd, int export_only, void* stream) {
+                 float lr, float wd, float mu, int export_only, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_apply, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, parity, lr, wd, export_only);
+                     static_cast<hipStream_t>(stream), d, prefix, n, parity, lr, wd, mu, export_only);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -23,7 +23,7 @@ from typing import Callable, Iterator
 import numpy as np
 
 # roles in the seed sequence
-ROLE_GRAD, ROLE_PARAM, ROLE_PREV_GRAD, ROLE_SPIKE_U, ROLE_SPIKE_V, ROLE_SHAPES, ROLE_MOM = range(7)
+ROLE_GRAD, ROLE_PARAM, ROLE_PREV_GRAD, ROLE_SPIKE_U, ROLE_SPIKE_V, ROLE_SHAPES, ROLE_MOM, ROLE_COL = range(8)
 
 
 # --------------------------------------------------------------------------
@@ -230,11 +230,15 @@ def iter_inputs(w: Workload, indices=None, step: int = 0, threads: int = 8,
 
 
 def adhoc_inputs(rows: int, cols: int, grad_dtype: str, seed: int, grad_std: float = 1.0,
-                 mom_std: float = 0.0, param_std: float = 0.02) -> MatrixInputs:
+                 mom_std: float = 0.0, param_std: float = 0.02,
+                 col_offset: float = 0.0) -> MatrixInputs:
     """Seeded inputs of any shape (edge-case tests): N(0, grad_std) gradient
-    (rounded to bf16 when asked), N(0, mom_std) momentum, N(0, param_std)
-    parameter.  Seeds live in their own range (workload key 1000)."""
+    plus, when col_offset > 0, an N(0, col_offset) offset per column (rounded
+    to bf16 when asked), N(0, mom_std) momentum, N(0, param_std) parameter.
+    Seeds live in their own range (workload key 1000)."""
     g = _normal(_rng(1000, seed, rows, cols, ROLE_GRAD), (rows, cols), grad_std)
+    if col_offset > 0:
+        g = (g + _normal(_rng(1000, seed, rows, cols, ROLE_COL), (1, cols), col_offset)).astype(np.float32)
     bits = None
     if grad_dtype == "bf16":
         bits = f32_to_bf16_bits(g)

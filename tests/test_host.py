@@ -211,3 +211,31 @@ def test_adamw_argument_errors_are_caught_on_the_host(lib):
     # no gradients: validated, nothing launched
     assert _acall(lib, _adam([dict(AGOOD, grad=0, step=0)]), 1) == muon.MUON_OK
     assert _acall(lib, ok, 0) == muon.MUON_OK
+
+
+def test_step_variant_options_are_validated(lib):
+    ok = _mats([GOOD])
+    c = (muon.MuonCoeff * 1)(muon.MuonCoeff(3.4445, -4.775, 2.0315))
+
+    def call(flags, reserved=0, ws_bytes=1 << 60):
+        opts = muon.MuonOptions(flags, reserved)
+        return lib.muon_step_ex(ok, 1, 0.02, 0.95, 0.0, 5, c, 1, 0, 1e-7, ctypes.byref(opts),
+                                ctypes.c_void_p(1 << 40), ws_bytes, None)
+
+    assert call(8) == muon.MUON_EINVAL                                   # unknown flag
+    assert call(muon.MUON_OPT_ZERO_CENTER, reserved=1) == muon.MUON_EINVAL
+    assert call(muon.MUON_OPT_NESTEROV | muon.MUON_OPT_NS_FIRST) == muon.MUON_EINVAL
+    # valid options still meet the workspace check before any launch
+    for f in (muon.MUON_OPT_ZERO_CENTER, muon.MUON_OPT_NESTEROV, muon.MUON_OPT_NS_FIRST,
+              muon.MUON_OPT_ZERO_CENTER | muon.MUON_OPT_NS_FIRST):
+        assert call(f, ws_bytes=16) == muon.MUON_EWORKSPACE
+    # NULL options: the plain step's validation
+    assert lib.muon_step_ex(ok, 1, 0.02, 0.95, 0.0, -1, c, 1, 0, 1e-7, None,
+                            ctypes.c_void_p(1 << 40), 1 << 60, None) == muon.MUON_EINVAL
+
+
+def test_workspace_reserves_column_sums(lib):
+    # the column-sum region sits between the table and the first X buffer
+    shapes = [(300, 2100), (7, 9)]
+    v0 = muon.workspace_view(shapes, 0, 5)
+    assert v0["x_off"][0] >= v0["nrm2_off"] + 16 + 8 * (2100 + 9)
