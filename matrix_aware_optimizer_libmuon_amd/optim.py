@@ -5,9 +5,11 @@ Interface of the optimizer class in "Muon meets Mamba" (wmrh.cn), sections
 4.1-4.3: parameter groups carry a ``muon`` flag (default True); Muon groups
 take 2-D hidden-layer weights, the others (1-D biases and norm weights,
 embeddings, heads) get the AdamW update with its own learning rate; weight
-decay is shared.  Each step issues one grouped ``muon_step`` per Muon group
-and one grouped ``muon_adamw_step`` per AdamW group; every per-element and
-per-matrix computation runs in libmuon.so.
+decay is shared.  The step variants (zero-centering of section 2.1, the
+look-ahead input, the Newton-Schulz-first order) are per-group switches.
+Each step issues one grouped ``muon_step`` per Muon group and one grouped
+``muon_adamw_step`` per AdamW group; every per-element and per-matrix
+computation runs in libmuon.so.
 
     opt = Muon([{"params": hidden_2d},
                 {"params": others, "muon": False}])
@@ -23,10 +25,12 @@ from . import QUINTIC, adamw_step, alloc_adamw_workspace, alloc_workspace, muon_
 class Muon(torch.optim.Optimizer):
     def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, ns_steps: int = 5,
                  adamw_lr: float = 1e-3, adamw_betas=(0.9, 0.95), adamw_eps: float = 1e-8,
-                 wd: float = 0.01, coeffs=QUINTIC, rms_scale: str | None = None, eps: float = 1e-7):
+                 wd: float = 0.01, coeffs=QUINTIC, rms_scale: str | None = None, eps: float = 1e-7,
+                 zero_centering: bool = False, nesterov: bool = False, ns_first: bool = False):
         defaults = dict(lr=lr, momentum=momentum, ns_steps=ns_steps, adamw_lr=adamw_lr,
                         adamw_betas=tuple(adamw_betas), adamw_eps=adamw_eps, wd=wd, coeffs=coeffs,
-                        rms_scale=rms_scale, eps=eps, muon=True)
+                        rms_scale=rms_scale, eps=eps, zero_centering=zero_centering,
+                        nesterov=nesterov, ns_first=ns_first, muon=True)
         super().__init__(params, defaults)
         for group in self.param_groups:
             for p in group["params"]:
@@ -70,7 +74,9 @@ class Muon(torch.optim.Optimizer):
         ws = self._workspace(("muon", gi, shapes), lambda: alloc_workspace(shapes, params[0].device))
         muon_step(params, [p.grad.contiguous() for p in params], moms, lr=group["lr"],
                   mu=group["momentum"], wd=group["wd"], ns_steps=group["ns_steps"],
-                  coeffs=group["coeffs"], rms_scale=group["rms_scale"], eps=group["eps"], workspace=ws)
+                  coeffs=group["coeffs"], rms_scale=group["rms_scale"], eps=group["eps"],
+                  zero_centering=group["zero_centering"], nesterov=group["nesterov"],
+                  ns_first=group["ns_first"], workspace=ws)
 
     def _step_adamw(self, gi, group):
         params = [p for p in group["params"] if p.grad is not None]

@@ -53,3 +53,25 @@ def test_hybrid_optimizer_two_steps_match_oracles():
 def test_muon_groups_take_only_2d_weights():
     with pytest.raises(ValueError):
         Muon([torch.nn.Parameter(torch.zeros(4, device=DEV))])
+
+
+@pytest.mark.parametrize("variant", [dict(zero_centering=True, nesterov=True),
+                                     dict(zero_centering=True, ns_first=True)])
+def test_optimizer_group_variants_match_oracle(variant):
+    lr, mu, wd = 0.02, 0.95, 0.01
+    hid = [W.adhoc_inputs(r, c, "f32", seed=600 + i, col_offset=0.5)
+           for i, (r, c) in enumerate([(192, 320), (320, 192)])]
+    ph = [torch.nn.Parameter(torch.from_numpy(h.param).to(DEV)) for h in hid]
+    opt = Muon([dict(params=ph, **variant)])
+    for p, h in zip(ph, hid):
+        p.grad = torch.from_numpy(h.grad).to(DEV)
+    opt.step()
+    torch.cuda.synchronize()
+    for p, h in zip(ph, hid):
+        out = oracle.muon_step_matrix(h.param, h.grad, np.zeros((h.rows, h.cols)), lr=lr, mu=mu,
+                                      wd=wd, ns_steps=5, **variant)
+        m = opt.state[p]["momentum_buffer"].cpu().numpy()
+        assert rel(m, out["m"]) <= (2e-2 if variant.get("ns_first") else 1e-5)
+        got = p.detach().cpu().numpy() - h.param.astype(np.float64) * (1.0 - lr * wd)
+        want = out["p"] - h.param.astype(np.float64) * (1.0 - lr * wd)
+        assert rel(got, want) <= 2e-2
