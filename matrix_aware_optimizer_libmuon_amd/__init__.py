@@ -37,24 +37,21 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
-    torch = _torch()
-    if t.dtype == torch.float32:
-        return MUON_F32
-    if t.dtype == torch.bfloat16:
-        return MUON_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+_MARSHAL = None
 
 
-def _check_2d(t, name: str, dtype=None):
-    if t.dim() != 2:
-        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+def _marshaller():
+    """The C++ marshalling module (fills descriptor arrays from tensor lists)."""
+    global _MARSHAL
+    if _MARSHAL is None:
+        _torch()  # its shared libraries must be loaded first
+        try:
+            from . import _marshal as m
+        except ImportError as e:
+            raise RuntimeError("the binding's marshalling module is not built; build it with "
+                               "`python -m matrix_aware_optimizer_libmuon_amd.build`") from e
+        _MARSHAL = m
+    return _MARSHAL
 
 
 def _coeff_array(coeffs, ns_steps: int):
@@ -128,28 +125,13 @@ def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 
     ``ns_first`` select the step variants of ``muon_step_ex``."""
     torch = _torch()
     n = len(params)
-    if len(grads) != n or len(moms) != n:
-        raise ValueError("params, grads and moms must have the same length")
     if rms_scale not in (None, "none", "sqrt_max1"):
         raise ValueError(f"unknown rms_scale {rms_scale!r}")
     mode = MUON_SCALE_SQRT_MAX1 if rms_scale == "sqrt_max1" else MUON_SCALE_NONE
     arr = (MuonMatrix * max(1, n))()
+    sc = [] if scales is None else [0.0 if s is None else float(s) for s in scales]
+    _marshaller().fill_matrices(params, grads, moms, sc, ctypes.addressof(arr))
     device = params[0].device if n else torch.device("cuda")
-    for i, (p, g, m) in enumerate(zip(params, grads, moms)):
-        _check_2d(p, f"params[{i}]", torch.float32)
-        _check_2d(m, f"moms[{i}]", torch.float32)
-        if m.shape != p.shape:
-            raise ValueError(f"moms[{i}] shape {tuple(m.shape)} != param shape {tuple(p.shape)}")
-        arr[i].param = p.data_ptr()
-        arr[i].momentum = m.data_ptr()
-        arr[i].rows, arr[i].cols = p.shape
-        arr[i].scale = float(scales[i]) if scales is not None and scales[i] is not None else 0.0
-        if g is not None:
-            _check_2d(g, f"grads[{i}]")
-            if g.shape != p.shape:
-                raise ValueError(f"grads[{i}] shape {tuple(g.shape)} != param shape {tuple(p.shape)}")
-            arr[i].grad = g.data_ptr()
-            arr[i].grad_dtype = _dtype_code(g)
     if workspace is None:
         workspace = alloc_workspace([tuple(p.shape) for p in params], device)
     carr, nc = _coeff_array(coeffs, ns_steps)
@@ -179,15 +161,7 @@ def orthogonalize(inputs: Sequence, outputs: Sequence | None = None, *, ns_steps
     if outputs is None:
         outputs = [torch.empty(t.shape, dtype=torch.bfloat16, device=t.device) for t in inputs]
     arr = (MuonOrtho * max(1, n))()
-    for i, (x, y) in enumerate(zip(inputs, outputs)):
-        _check_2d(x, f"inputs[{i}]")
-        _check_2d(y, f"outputs[{i}]", torch.bfloat16)
-        if y.shape != x.shape:
-            raise ValueError(f"outputs[{i}] shape mismatch")
-        arr[i].inp = x.data_ptr()
-        arr[i].out = y.data_ptr()
-        arr[i].rows, arr[i].cols = x.shape
-        arr[i].in_dtype = _dtype_code(x)
+    _marshaller().fill_ortho(inputs, outputs, ctypes.addressof(arr))
     if workspace is None:
         workspace = alloc_workspace([tuple(t.shape) for t in inputs], device)
     carr, nc = _coeff_array(coeffs, ns_steps)
@@ -225,24 +199,10 @@ def adamw_step(params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg_sq
     it.  Returns the workspace used."""
     torch = _torch()
     n = len(params)
-    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == len(steps) == n):
-        raise ValueError("params, grads, exp_avgs, exp_avg_sqs and steps must have the same length")
     arr = (MuonAdamWTensor * max(1, n))()
+    _marshaller().fill_adamw(params, grads, exp_avgs, exp_avg_sqs, [int(t) for t in steps],
+                          ctypes.addressof(arr))
     device = params[0].device if n else torch.device("cuda")
-    for i, (p, g, m, v, t) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs, steps)):
-        for name, x in (("params", p), ("exp_avgs", m), ("exp_avg_sqs", v)):
-            if not x.is_cuda or not x.is_contiguous() or x.dtype != torch.float32:
-                raise ValueError(f"{name}[{i}] must be a contiguous fp32 GPU tensor")
-        if m.shape != p.shape or v.shape != p.shape:
-            raise ValueError(f"moment shapes of tensor {i} differ from the param's")
-        arr[i].param, arr[i].exp_avg, arr[i].exp_avg_sq = p.data_ptr(), m.data_ptr(), v.data_ptr()
-        arr[i].numel = p.numel()
-        arr[i].step = int(t)
-        if g is not None:
-            if not g.is_cuda or not g.is_contiguous() or g.shape != p.shape:
-                raise ValueError(f"grads[{i}] must be a contiguous GPU tensor shaped like its param")
-            arr[i].grad = g.data_ptr()
-            arr[i].grad_dtype = _dtype_code(g)
     if workspace is None:
         workspace = alloc_adamw_workspace(n, device)
     st = _lib.load().muon_adamw_step(arr, n, float(lr), float(betas[0]), float(betas[1]), float(eps),

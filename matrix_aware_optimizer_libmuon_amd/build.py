@@ -1,4 +1,5 @@
-"""Build libmuon.so (gfx950) in place with hipcc.
+"""Build libmuon.so (gfx950) in place with hipcc, and the binding's argument
+marshalling module (_marshal, plain C++ against torch's headers, g++).
 
     python -m matrix_aware_optimizer_libmuon_amd.build
 """
@@ -7,6 +8,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import sysconfig
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -33,27 +35,63 @@ FLAGS = [
 ]
 
 
-def _run(cmd, verbose):
+MARSHAL = os.path.join(PKG, "_marshal" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def _start(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    return cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(job, verbose):
+    cmd, proc = job
+    out, _ = proc.communicate()
+    out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"{os.path.basename(cmd[0])} failed ({proc.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
 
 
+def _run(cmd, verbose):
+    _finish(_start(cmd, verbose), verbose)
+
+
+def _marshal_cmd(out):
+    from torch.utils import cpp_extension as ce
+    import torch
+    abi = int(torch._C._GLIBCXX_USE_CXX11_ABI)
+    libdir = ce.library_paths()[0]
+    return ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-Wall",
+            f"-D_GLIBCXX_USE_CXX11_ABI={abi}", "-DTORCH_EXTENSION_NAME=_marshal",
+            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+            *[f"-I{p}" for p in ce.include_paths()], f"-I{sysconfig.get_paths()['include']}",
+            os.path.join(CSRC, "marshal.cpp"), "-o", out,
+            f"-L{libdir}", "-lc10", "-ltorch", "-ltorch_cpu", "-ltorch_python", f"-Wl,-rpath,{libdir}"]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libmuon.so next to this file; returns its path."""
+    """Compile every source (in parallel), link libmuon.so next to this file
+    and build the marshalling module; returns the library's path."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    jobs, objs = [], []
     for src, extra in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC, *FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)
+        jobs.append(_start([HIPCC, *FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], verbose))
         objs.append(obj)
+    marshal_tmp = MARSHAL + ".tmp"
+    jobs.append(_start(_marshal_cmd(marshal_tmp), verbose))
+    try:
+        for job in jobs:
+            _finish(job, verbose)
+    finally:
+        for _, proc in jobs:
+            if proc.poll() is None:
+                proc.kill()
+                proc.wait()
+    os.replace(marshal_tmp, MARSHAL)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

@@ -239,3 +239,32 @@ def test_workspace_reserves_column_sums(lib):
     shapes = [(300, 2100), (7, 9)]
     v0 = muon.workspace_view(shapes, 0, 5)
     assert v0["x_off"][0] >= v0["nrm2_off"] + 16 + 8 * (2100 + 9)
+
+
+def test_marshalling_module_matches_the_header(lib):
+    m = muon._marshaller()
+    assert m.MATRIX_BYTES == ctypes.sizeof(muon.MuonMatrix)
+    assert m.ORTHO_BYTES == ctypes.sizeof(muon.MuonOrtho)
+    assert m.ADAMW_BYTES == ctypes.sizeof(muon.MuonAdamWTensor)
+
+
+def test_marshalling_rejects_bad_tensors(lib):
+    torch = pytest.importorskip("torch")
+    m = muon._marshaller()
+    arr = (muon.MuonMatrix * 2)()
+    p = torch.zeros(4, 4)
+    with pytest.raises(ValueError, match="same length"):
+        m.fill_matrices([p], [p, p], [p], [], ctypes.addressof(arr))
+    with pytest.raises(ValueError, match="scales"):
+        m.fill_matrices([p], [p], [p], [1.0, 2.0], ctypes.addressof(arr))
+    with pytest.raises(ValueError, match=r"params\[0\] must be 2-D"):
+        m.fill_matrices([torch.zeros(4)], [None], [torch.zeros(4)], [], ctypes.addressof(arr))
+    with pytest.raises(ValueError, match=r"params\[0\] must be contiguous"):
+        m.fill_matrices([p.t()[:, :2]], [None], [p], [], ctypes.addressof(arr))
+    with pytest.raises(ValueError, match="GPU"):
+        m.fill_matrices([p], [p], [p], [], ctypes.addressof(arr))
+    with pytest.raises(ValueError, match="same length"):
+        m.fill_adamw([p], [p], [p], [p], [1, 2], ctypes.addressof(arr))
+    with pytest.raises(ValueError, match="same length"):
+        m.fill_ortho([p], [], ctypes.addressof(arr))
+    assert m.fill_matrices([], [], [], [], ctypes.addressof(arr)) is None
