@@ -33,33 +33,42 @@ METRIC = "Muon step NS TFLOP/s + matrices/s at 1 GPU; % of bf16 MFMA peak"
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 QUINTIC = (3.4445, -4.7750, 2.0315)
+FUSED_TILE = 32                 # padding granule the library reports for the fused class
+NS_PHASES = ("gram", "gram2_epilogue", "x_update", "ns_fused")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def phase_work(w):
+def phase_work(w, muon):
     """Algorithmic work of one launch of each phase over the workload:
     flops for the MFMA phases (per Newton-Schulz iteration: X X^T 2 m^2 n,
-    A A 2 m^3, B X 2 m^2 n), HBM bytes for the elementwise ones (momentum:
-    read G and M, write M; normalise: read M, write bf16 X0; apply: read p
-    and bf16 O, write p)."""
-    gram = gram2 = xupd = 0
+    A A 2 m^3, C X 2 m^2 n; the fused launch runs every iteration of the
+    small matrices, the tiled ones one iteration of the others), HBM bytes
+    for the elementwise ones (momentum: read G and M, write M; normalise:
+    read M, write bf16 X0; apply: read p and bf16 O, write p)."""
+    gram = gram2 = xupd = fused = 0
     b_mom = b_norm = b_apply = 0
     gsz = 2 if w.grad_dtype == "bf16" else 4
+    cls = {}
     for r, c in w.shapes:
+        if (r, c) not in cls:  # the kernel class depends on the shape alone
+            cls[(r, c)] = muon.workspace_view([(r, c)], 0, w.ns_steps)["tile"]
         m, n = min(r, c), max(r, c)
-        gram += 2 * m * m * n
-        gram2 += 2 * m ** 3
-        xupd += 2 * m * m * n
+        if cls[(r, c)] == FUSED_TILE:
+            fused += w.ns_steps * (4 * m * m * n + 2 * m ** 3)
+        else:
+            gram += 2 * m * m * n
+            gram2 += 2 * m ** 3
+            xupd += 2 * m * m * n
         e = r * c
         b_mom += e * (gsz + 8)
         b_norm += e * (4 + 2)
         b_apply += e * (4 + 2 + 4)
     return {"momentum_norm": ("hbm", b_mom), "normalize_cast": ("hbm", b_norm),
             "gram": ("mfma", gram), "gram2_epilogue": ("mfma", gram2),
-            "x_update": ("mfma", xupd), "apply": ("hbm", b_apply)}
+            "x_update": ("mfma", xupd), "apply": ("hbm", b_apply), "ns_fused": ("mfma", fused)}
 
 
 def cpu_baseline(w, target_s: float = 20.0):
@@ -221,7 +230,7 @@ def main():
            "nominal_ns_flops_per_step": flops_step}
 
     if phases is not None:
-        work = phase_work(w)
+        work = phase_work(w, muon)
         per = {}
         for name, rec in phases.items():
             n = rec["launches"]
@@ -241,7 +250,7 @@ def main():
                              "bound": "hbm", "achieved": achieved, "unit": "GB/s",
                              "peak": HBM_PEAK_GBS, "frac": achieved / HBM_PEAK_GBS,
                              "algorithmic_per_launch": amount}
-        ns_ms = sum(phases[k]["ms"] for k in ("gram", "gram2_epilogue", "x_update")) / args.steps
+        ns_ms = sum(phases[k]["ms"] for k in NS_PHASES) / args.steps
         out["ns_ms_per_step"] = ns_ms
         out["ns_tflops"] = flops_step / (ns_ms / 1e3) / 1e12
         out["ns_frac_of_bf16_peak"] = out["ns_tflops"] / BF16_PEAK_TFLOPS

@@ -110,8 +110,12 @@ typedef struct { float a, b, c; } muon_ns_coeff_t;
 size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n_mats);
 
 /* One Muon step over a list of matrices, as grouped launches: one launch per
- * phase covers every matrix (3 + 3 * ns_steps launches in all), whatever
- * their number and shapes.
+ * phase covers every matrix, whatever their number and shapes.  Matrices
+ * whose whole iteration fits one workgroup's LDS (short side <= 128 and, with
+ * both sides padded to 32, m x n + 2 m x m bf16 within 160 KB) run every
+ * Newton-Schulz step in one fused launch; the others take three launches per
+ * step (Gram, C, X update) by tile class.  In all at most 4 + 3 * ns_steps
+ * launches (one more with zero-centering).
  *   lr, mu, wd   learning rate, momentum, decoupled weight decay (finite).
  *   ns_steps     0 .. MUON_MAX_NS_STEPS Newton-Schulz iterations.
  *   coeffs       n_coeffs triples: 1 (used for every step) or ns_steps (one
@@ -208,7 +212,8 @@ typedef struct {
   int64_t cols_pad;
   int64_t m_pad;
   int32_t transposed;   /* 1 when rows > cols: the iteration runs on X^T */
-  int32_t tile;         /* padding granule of this matrix                 */
+  int32_t tile;         /* padding granule: 256 or 128 (tiled kernels) or
+                           32 (the fused small-matrix iteration)           */
 } muon_workspace_view_t;
 
 int muon_workspace_view(const muon_matrix_t* mats, int64_t n_mats, int64_t index,
@@ -260,8 +265,9 @@ int muon_adamw_step(const muon_adamw_tensor_t* tensors, int64_t n_tensors, float
  * counts per phase (MUON_PHASES entries each; either pointer may be NULL) and
  * clears the record.  Phases: momentum+norm, normalise+cast, Gram X X^T,
  * Gram A A with the b A + c A^2 epilogue, X update, apply (or export),
- * AdamW. */
-#define MUON_PHASES 7
+ * AdamW, and the fused iteration of small matrices (every Newton-Schulz
+ * step of each matrix whose whole iteration fits one workgroup's LDS). */
+#define MUON_PHASES 8
 int muon_timing_enable(int on);
 int muon_timing_read(double* ms, int64_t* launches);
 

@@ -28,9 +28,9 @@ MUON_OPT_ZERO_CENTER = 1
 MUON_OPT_NESTEROV = 2
 MUON_OPT_NS_FIRST = 4
 
-MUON_PHASES = 7
+MUON_PHASES = 8
 PHASE_NAMES = ("momentum_norm", "normalize_cast", "gram", "gram2_epilogue", "x_update", "apply",
-               "adamw")
+               "adamw", "ns_fused")
 
 EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_step_ex", "muon_orthogonalize",
             "muon_workspace_view",

@@ -21,6 +21,7 @@ SOURCES = [
     ("muon_kernels.hip", []),
     ("muon_gemm256.hip", []),
     ("muon_gemm128.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
+    ("muon_fused.hip", []),
     ("muon_api.cpp", []),
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

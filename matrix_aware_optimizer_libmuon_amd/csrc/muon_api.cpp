@@ -29,7 +29,8 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 // workspace plan (a pure function of the shapes)
 //
-//   [ table: MatDesc[n] | 8 prefix arrays int64[n+1] | nrm2 double[n] ] (256-aligned)
+//   [ table: MatDesc[n] | 8 prefix arrays int64[n+1] | nrm2 double[n] |
+//     NS coefficients float[3 * MUON_MAX_NS_STEPS] ] (256-aligned)
 //   [ column sums: double[cols] per matrix ] (256-aligned; zero-centering only)
 //   then, per matrix (all n, skipped ones included):
 //   [ X0 | X1 ] rows_pad x cols_pad bf16 each, [ A | C ] m_pad x m_pad bf16 each,
@@ -41,7 +42,22 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 enum { kPreFlat = 0, kPrePad = 1, kPreSymBig = 2, kPreFullBig = 3, kPreSymSmall = 4,
        kPreFullSmall = 5, kPreRows = 6, kPreCol = 7, kNumPrefix = 8 };
 
-int tile_class(int64_t r, int64_t c) { return std::min(r, c) >= kBigMinM ? kTileBig : kTileSmall; }
+int64_t ceil_to(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// LDS bytes the fused kernel needs for an r x c matrix (0: not eligible).
+int64_t fused_lds(int64_t r, int64_t c) {
+  const int64_t m = ceil_to(std::min(r, c), kTileFused), n = ceil_to(std::max(r, c), kTileFused);
+  if (m > kFusedMaxM) return 0;
+  const int64_t bytes = 2 * (m * ceil_to(n, 128) + 2 * m * ceil_to(m, 128));
+  return bytes <= kFusedLdsMax ? bytes : 0;
+}
+
+// Padding granule / kernel class of a matrix: 256 or 128 (tiled GEMM
+// launches) or kTileFused (the whole iteration in one workgroup).
+int tile_class(int64_t r, int64_t c) {
+  if (std::min(r, c) >= kBigMinM) return kTileBig;
+  return fused_lds(r, c) ? kTileFused : kTileSmall;
+}
 
 struct MatPlan {
   int64_t rows, cols, rows_pad, cols_pad, m_pad, n_pad;
@@ -52,7 +68,7 @@ struct MatPlan {
 
 struct Plan {
   int64_t n = 0;
-  size_t desc_off = 0, prefix_off[kNumPrefix] = {}, nrm2_off = 0, table_bytes = 0;
+  size_t desc_off = 0, prefix_off[kNumPrefix] = {}, nrm2_off = 0, coeff_off = 0, table_bytes = 0;
   size_t colsum_off = 0;
   int64_t colsum_count = 0;           // doubles in the column-sum region
   size_t total = 0;
@@ -73,6 +89,8 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
   }
   plan.nrm2_off = off;
   off += static_cast<size_t>(n) * sizeof(double);
+  plan.coeff_off = off;
+  off += 3 * MUON_MAX_NS_STEPS * sizeof(float);
   plan.table_bytes = align_up(off, kAlign);
   plan.mats.resize(static_cast<size_t>(n));
   plan.colsum_off = plan.table_bytes;
@@ -229,7 +247,11 @@ int timed(int phase, hipStream_t stream, F&& launch) {
 struct Table {
   std::vector<unsigned char> bytes;
   int n_active = 0;
-  int n_big = 0;                      // descriptors [0, n_big) are 256-tile matrices
+  int n_big = 0;                      // descriptors [0, n_big): 256-tile matrices,
+  int n_small = 0;                    // then n_small 128-tile ones,
+  int n_fused = 0;                    // then n_fused fused-kernel ones, by padded
+  int fused_n[4] = {};                // short side 32, 64, 96, 128: counts and
+  int fused_lds[4] = {};              // largest LDS need per class
   int64_t units[kNumPrefix] = {};
 };
 
@@ -257,7 +279,8 @@ bool any_overlap(std::vector<std::pair<uintptr_t, uintptr_t>>& r) {
 }
 
 // Fill the descriptor table for the active matrices: 256-tile matrices first,
-// then 128-tile ones, so each GEMM class is one contiguous descriptor range.
+// then 128-tile ones, then the fused class, so each class is one contiguous
+// descriptor range.
 template <class Fill>
 void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) {
   const size_t n = static_cast<size_t>(plan.n);
@@ -269,14 +292,16 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
     pre[k] = reinterpret_cast<int64_t*>(t.bytes.data() + plan.prefix_off[k]);
   int64_t acc[kNumPrefix] = {};
   int a = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int want = pass == 0 ? kTileBig : kTileSmall;
+  // passes: 256 class, 128 class, then the fused class by padded short side
+  for (int pass = 0; pass < 6; ++pass) {
+    const int want = pass == 0 ? kTileBig : pass == 1 ? kTileSmall : kTileFused;
+    const int fm = kTileFused * (pass - 1);   // fused passes: m_pad 32, 64, 96, 128
     const int sym = pass == 0 ? kPreSymBig : kPreSymSmall;
     const int full = pass == 0 ? kPreFullBig : kPreFullSmall;
     int local = 0;
     for (size_t i = 0; i < n; ++i) {
       const MatPlan& m = plan.mats[i];
-      if (m.tile != want) continue;
+      if (m.tile != want || (pass >= 2 && m.m_pad != fm)) continue;
       MatDesc d;
       std::memset(&d, 0, sizeof(d));
       if (!fill(i, d)) continue;
@@ -311,16 +336,28 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
       pre[kPreCol][a] = acc[kPreCol];
       if (d.flags & kFlagZeroCenter)
         acc[kPreCol] += ((m.rows + kColRows - 1) / kColRows) * ((m.cols + kColCols - 1) / kColCols);
-      pre[sym][local] = acc[sym];
-      acc[sym] += t_side * (t_side + 1) / 2;
-      pre[full][local] = acc[full];
-      acc[full] += (m.rows_pad / m.tile) * (m.cols_pad / m.tile);
+      if (pass < 2) {
+        pre[sym][local] = acc[sym];
+        acc[sym] += t_side * (t_side + 1) / 2;
+        pre[full][local] = acc[full];
+        acc[full] += (m.rows_pad / m.tile) * (m.cols_pad / m.tile);
+      } else {
+        int& l = t.fused_lds[pass - 2];
+        l = std::max(l, static_cast<int>(fused_lds(m.rows, m.cols)));
+      }
       ++a;
       ++local;
     }
-    pre[sym][local] = acc[sym];
-    pre[full][local] = acc[full];
+    if (pass < 2) {
+      pre[sym][local] = acc[sym];
+      pre[full][local] = acc[full];
+    }
     if (pass == 0) t.n_big = local;
+    if (pass == 1) t.n_small = local;
+    if (pass >= 2) {
+      t.fused_n[pass - 2] = local;
+      t.n_fused += local;
+    }
   }
   pre[kPreFlat][a] = acc[kPreFlat];
   pre[kPrePad][a] = acc[kPrePad];
@@ -329,17 +366,25 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
   for (int k = 0; k < kNumPrefix; ++k) t.units[k] = acc[k];
 }
 
-int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float lr, float mu,
+int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, float mu,
                  float wd, int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, float eps,
                  hipStream_t stream) {
+  // the coefficients travel with the table (the fused kernel reads them)
+  float* cf = reinterpret_cast<float*>(t.bytes.data() + plan.coeff_off);
+  for (int k = 0; k < (ns_steps > 0 ? n_coeffs : 0); ++k) {
+    cf[3 * k] = coeffs[k].a;
+    cf[3 * k + 1] = coeffs[k].b;
+    cf[3 * k + 2] = coeffs[k].c;
+  }
   int rc = upload_table(t.bytes.data(), t.bytes.size(), ws, stream);
   if (rc != MUON_OK) return rc;
   if (t.n_active == 0) return MUON_OK;
   const MatDesc* d = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
   const int64_t* pre[kNumPrefix];
   for (int k = 0; k < kNumPrefix; ++k) pre[k] = reinterpret_cast<const int64_t*>(ws + plan.prefix_off[k]);
-  const int n = t.n_active, nb = t.n_big, ns = n - nb;
+  const int n = t.n_active, nb = t.n_big, ns = t.n_small, nf = t.n_fused;
   const MatDesc* d_small = d + nb;
+  const MatDesc* d_fused = d + nb + ns;
   void* s = static_cast<void*>(stream);
   if (t.units[kPreCol] > 0) {
     // zero-centering: column sums of G first (counted with the momentum phase)
@@ -357,7 +402,19 @@ int run_sequence(const Plan& plan, const Table& t, char* ws, bool ortho, float l
     return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, mu, s);
   });
   if (rc) return rc;
-  for (int k = 0; k < ns_steps; ++k) {
+  const MatDesc* df = d_fused;
+  for (int c = 0; c < 4 && nf > 0 && ns_steps > 0; ++c) {
+    const int cnt = t.fused_n[c];
+    if (cnt == 0) continue;
+    rc = timed(kPhaseFusedNS, stream, [&] {
+      return launch_ns_fused(kTileFused * (c + 1), df, cnt,
+                             reinterpret_cast<const float*>(ws + plan.coeff_off), n_coeffs,
+                             ns_steps, t.fused_lds[c], s);
+    });
+    if (rc) return rc;
+    df += cnt;
+  }
+  for (int k = 0; k < ((nb + ns) > 0 ? ns_steps : 0); ++k) {
     const muon_ns_coeff_t& c = coeffs[n_coeffs == 1 ? 0 : k];
     const int parity = k & 1;
     rc = timed(kPhaseGram, stream, [&] {

@@ -19,6 +19,13 @@ namespace muon {
 constexpr int kTileSmall = 128;
 constexpr int kTileBig = 256;
 constexpr int kBigMinM = 1024;
+// Small matrices whose whole iteration fits in LDS take the fused kernel
+// (muon_fused.hip): both sides padded to kTileFused, short side at most
+// kFusedMaxM, and X plus two m x m buffers (LDS rows rounded up to 128
+// elements) within kFusedLdsMax bytes.
+constexpr int kTileFused = 32;
+constexpr int kFusedMaxM = 128;
+constexpr int kFusedLdsMax = 160 * 1024;
 // Elements handled by one workgroup of the elementwise phases.
 constexpr int kChunk = 16384;
 constexpr int kEwThreads = 256;
@@ -32,7 +39,8 @@ enum Phase : int {
   kPhaseXUpdate = 4,
   kPhaseApply = 5,
   kPhaseAdamW = 6,
-  kNumPhases = 7
+  kPhaseFusedNS = 7,
+  kNumPhases = 8
 };
 
 // flags of MatDesc
@@ -114,6 +122,11 @@ int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, 
                  float lr, float wd, float mu, int export_only, void* stream);
 int launch_adamw(const AdamDesc* d, const int64_t* prefix, int n, int64_t units, float beta1,
                  float beta2, float eps, void* stream);
+// fused iteration (muon_fused.hip): one workgroup per descriptor d[0 .. n),
+// all of padded short side m_pad (32, 64, 96 or 128); coeffs = 3 floats per
+// step on the device; lds_bytes = the largest need among them
+int launch_ns_fused(int m_pad, const MatDesc* d, int n, const float* coeffs, int n_coeffs,
+                    int ns_steps, int lds_bytes, void* stream);
 
 // per-tile GEMM launchers (muon_gemm256.hip, muon_gemm128.hip)
 int launch_gram_256(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,

@@ -22,7 +22,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = ("muon_device.h", "muon_internal.h", "muon_kernels.hip", "muon_gemm.h",
-                  "muon_gemm256.hip", "muon_gemm128.hip")
+                  "muon_gemm256.hip", "muon_gemm128.hip", "muon_fused.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "muon_step_transformer_d4096_hbm_traffic.md")
 
 # kernel symbol -> bench phase name

@@ -114,7 +114,8 @@ def test_grouped_dispatch_equals_one_by_one_and_is_order_free():
 
 
 @pytest.mark.parametrize("shape", [(200, 300), (300, 200), (256, 256), (40, 600), (600, 100),
-                                   (1024, 1536), (1536, 1024), (1100, 1100)])
+                                   (1024, 1536), (1536, 1024), (1100, 1100),
+                                   (17, 15), (300, 100), (64, 1024)])
 def test_stage_consistency_of_the_gemm_kernels(shape):
     """One iteration (ns = 1) read stage by stage from the workspace: every
     bf16 result is the round-to-nearest of the exact value computed from the

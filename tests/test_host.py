@@ -268,3 +268,23 @@ def test_marshalling_rejects_bad_tensors(lib):
     with pytest.raises(ValueError, match="same length"):
         m.fill_ortho([p], [], ctypes.addressof(arr))
     assert m.fill_matrices([], [], [], [], ctypes.addressof(arr)) is None
+
+
+def test_kernel_class_by_shape(lib):
+    # fused: short side <= 128 and, padded to 32 with LDS rows of 128
+    # elements, m n + 2 m m bf16 within 160 KB; 256 from a short side of 1024
+    def tile(r, c):
+        return muon.workspace_view([(r, c)], 0, 5)["tile"]
+
+    def lds(r, c):
+        m, n = -(-min(r, c) // 32) * 32, -(-max(r, c) // 32) * 32
+        return 2 * (m * (-(-n // 128) * 128) + 2 * m * (-(-m // 128) * 128))
+
+    for r, c in [(1, 1), (1, 40), (40, 1), (17, 15), (64, 1024), (1024, 64), (100, 300),
+                 (300, 100), (128, 256), (48, 1000), (32, 2304)]:
+        assert lds(r, c) <= 160 * 1024 and tile(r, c) == 32, (r, c)
+    for r, c in [(64, 1056), (129, 257), (128, 512), (48, 1536), (1536, 80), (256, 768)]:
+        assert tile(r, c) == 128, (r, c)
+    assert tile(1024, 1024) == 256 and tile(4096, 14336) == 256
+    v = muon.workspace_view([(100, 300)], 0, 5)
+    assert (v["rows_pad"], v["cols_pad"], v["m_pad"]) == (128, 320, 128)
