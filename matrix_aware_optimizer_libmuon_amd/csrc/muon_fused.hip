@@ -20,14 +20,15 @@
 // LDS layout: X as [m][ldx] (the logical m x n orientation: a tall matrix is
 // transposed on the way in and out), P = A and later C_hi as [m][lda], Q =
 // C_lo as [m][lda]; ldx, lda = the widths rounded up to 128 elements.  The
-// 16-byte chunk c of row r sits at c ^ fsw(r), which makes both read forms
-// conflict-free:
-//   row fragments (16 rows, one 16-byte chunk each): fsw takes all 16 values
-//     over 16 consecutive rows, so the 16 lanes served per cycle hit
-//     distinct 16-byte bank groups;
-//   transposing column fragments (ds_read_b64_tr_b16: 4 consecutive rows x
-//     32 bytes per 16 lanes): fsw >> 1 differs over each aligned group of 4
-//     rows, so the four 32-byte pieces fall on distinct banks.
+// 16-byte chunk c of row r sits at c ^ fsw(r), fsw(r) = 2 (r & 3) + 8 ((r >> 3)
+// & 1), which makes both read forms conflict-free on the gfx950 LDS (64 banks
+// of 4 bytes; a 16-byte read serves each half-wave in two cycles, lanes
+// {0-3, 8-11, 20-23, 28-31} then the rest; a transposing 8-byte read serves
+// 32 consecutive lanes per cycle; measured with the bank-conflict counter):
+//   row fragments (lane l: row l & 15, chunk c + (l >> 4)): in each cycle the
+//     even and the odd chunk of the pair land on all 16 bank groups;
+//   column fragments (k rows 8 (l >> 4) + (l & 15) / 4, 32 bytes each): the 8
+//     rows of one cycle have distinct fsw >> 1, i.e. distinct 32-byte spans.
 #include <hip/hip_runtime.h>
 
 #include "muon_device.h"
@@ -40,7 +41,7 @@ typedef short v4i16f __attribute__((ext_vector_type(4)));
 constexpr int kFThreads = 512;  // 8 waves
 constexpr int kFWaves = kFThreads / 64;
 
-__device__ __forceinline__ int fsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int fsw(int r) { return ((r & 3) << 1) | (r & 8); }
 
 // element offset of logical (r, c) in a swizzled LDS buffer with row length ld
 __device__ __forceinline__ int spos(int r, int c, int ld) {

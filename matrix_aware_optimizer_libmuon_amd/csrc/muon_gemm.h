@@ -36,16 +36,20 @@ namespace muon {
 // "MN-contiguous" (element (mn, k) at p[k * ld + mn]).
 //   K-contiguous tiles sit in LDS as [mn][32 k] (64-byte rows); fragments
 //     are 16-byte reads; the 16-byte chunk c of row r is stored at
-//     c ^ ((r >> 2) & 3).  The LDS has 64 banks of 4 bytes and serves 16
-//     lanes of a 16-byte read per cycle: the 16 rows read together then
-//     cover all banks once (rows r and r + 4 share a 256-byte bank window
-//     and differ in the XOR term).
+//     c ^ (2 ((r >> 3) & 1)).
 //   MN-contiguous tiles keep their memory layout, [k][TILE mn]; fragments
 //     are assembled by the LDS transpose read (ds_read_b64_tr_b16: in each
 //     16-lane group, lane 4a + b receives element b of the 8-byte blocks
 //     addressed by lanes a, a + 4, a + 8, a + 12), so the transpose of a tall
 //     matrix is never materialised.  The 16-byte chunk c of k row r is
-//     stored at c ^ (2 (r & 3)).
+//     stored at c ^ (2 (r & 3) + 8 ((r >> 3) & 1)).
+// Both swizzles follow how the gfx950 LDS (64 banks of 4 bytes) serves the
+// two read forms, as measured with its bank-conflict counter: a 16-byte
+// read takes each half-wave in two cycles, lanes {0-3, 8-11, 20-23, 28-31}
+// then {4-7, 12-15, 16-19, 24-27} (mod 32); a transposing 8-byte read
+// takes 32 consecutive lanes per cycle.  For a fragment (lane l: row
+// l & 15, chunk l >> 4; or k rows 8 (l >> 4) + (l & 15) / 4 for the
+// transpose) each cycle then touches every bank once.
 // ---------------------------------------------------------------------------
 constexpr int BK = 32;
 constexpr int kStages = 4;
@@ -104,10 +108,11 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint16_t
 // is read at the wave-uniform base + kt kstep + q qstride plus a per-lane
 // 32-bit offset, so the loads need one or two address registers in all.
 //   K-contiguous: a block is 16 rows of 64 bytes; lane l reads row l / 4,
-//     chunk (l % 4) ^ ((row >> 2) & 3) (the stored swizzle; the XOR term
+//     chunk (l % 4) ^ (2 ((row >> 3) & 1)) (the stored swizzle; the XOR term
 //     depends on l only, since blocks start at multiples of 16 rows).
 //   MN-contiguous: a block is 512 / TILE k rows of 2 TILE bytes; lane l reads
-//     k row l / CPR, chunk (l % CPR) ^ (2 (row & 3)), which at TILE = 256
+//     k row r = R b + l / CPR, chunk (l % CPR) ^ (2 (r & 3) + 8 ((r >> 3) & 1));
+//     bit 3 of r is the parity of the wave, and at TILE = 256 r & 3 also
 //     depends on the parity of the block: two offsets.
 template <bool MN, int TILE>
 struct DmaFeed {
@@ -121,7 +126,7 @@ struct DmaFeed {
     const int64_t ldb = op.ld * 2;
     const char* p = reinterpret_cast<const char*>(op.p);
     if constexpr (!MN) {
-      const int row = lane >> 2, c = (lane & 3) ^ ((lane >> 4) & 3);
+      const int row = lane >> 2, c = (lane & 3) ^ (2 * ((row >> 3) & 1));
       voff[0] = voff[1] = static_cast<uint32_t>(row * ldb + 16 * c);
       base = p + (mn0 + 16 * LPW * w) * ldb;
       qstride = 16 * ldb;
@@ -131,7 +136,7 @@ struct DmaFeed {
       const int row = lane / CPR;
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
-        const int c = (lane % CPR) ^ (2 * ((R * par + row) & 3));
+        const int c = (lane % CPR) ^ (2 * ((R * par + row) & 3) + 8 * (w & 1));
         voff[par] = static_cast<uint32_t>(row * ldb + 16 * c);
       }
       base = p + (R * LPW * w) * ldb + mn0 * 2;
@@ -153,7 +158,7 @@ __device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase) {
   const int lane = threadIdx.x & 63;
   if constexpr (!MN) {
     const int row = rowbase + (lane & 15);
-    const int c = (lane >> 4) ^ ((row >> 2) & 3);
+    const int c = (lane >> 4) ^ (2 * ((row >> 3) & 1));
     return *reinterpret_cast<const bf16x8_t*>(tile + row * BK + c * 8);
   } else {
     // transpose reads: address lane j of a 16-lane group covers k row
@@ -162,7 +167,7 @@ __device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase) {
     const int g = lane >> 4, i = lane & 15;
     const int m = rowbase + 4 * (i & 3);
     const int k = 8 * g + (i >> 2);                      // + 4 below; k & 3 == i >> 2
-    const int off = (((m >> 3) ^ (2 * (i >> 2))) << 3) + (m & 4);
+    const int off = (((m >> 3) ^ (2 * (i >> 2) + 8 * (g & 1))) << 3) + (m & 4);
     const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16*)(tile + k * TILE + off));
     const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
