@@ -55,17 +55,21 @@ def trace_summary(stats_csv: str, title: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def _per_kernel(csv_path: str) -> dict:
+def _per_kernel(csv_path: str, reduce=None) -> dict:
     acc = defaultdict(list)
     for r in csv.DictReader(open(csv_path)):
         acc[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+    return {k: (reduce(v) if reduce else sum(v) / len(v)) for k, v in acc.items()}
 
 
 def traffic_summary(fetch_csv: str, write_csv: str, title: str, commands: str,
                     copy_bytes: int = 4 << 30) -> str:
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
     copy = "__amd_rocclr_copyBuffer"
+    # the calibration copy is the largest copy dispatch of the run (small
+    # ones are descriptor uploads)
+    fetch[copy] = _per_kernel(fetch_csv, max)[copy]
+    write[copy] = _per_kernel(write_csv, max)[copy]
     f_scale = copy_bytes / (fetch[copy] * 1024.0)
     w_scale = copy_bytes / (write[copy] * 1024.0)
     out = [f"# {title}", "", "Commands (repository root, one MI355X; one counter per run):", "", "```",

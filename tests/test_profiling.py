@@ -28,3 +28,26 @@ def test_hash_covers_every_kernel_source():
     csrc = os.path.join(profiling.PKG, "csrc")
     kernels = {f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))}
     assert kernels == set(profiling.KERNEL_SOURCES)
+
+
+def _counters(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (k, v) in enumerate(rows):
+            f.write(f"{i},{k},{counter},{v}\n")
+    return str(path)
+
+
+def test_traffic_calibrates_on_the_largest_copy(tmp_path):
+    # small descriptor uploads beside the 4 GiB calibration copy must not
+    # dilute the factors; kernels are averaged over their dispatches
+    copy = "__amd_rocclr_copyBuffer"
+    f = _counters(tmp_path / "f.csv", "FETCH_SIZE",
+                  [(copy, 1.0), (copy, 2 * 1024 * 1024.0), (copy, 3.0), ("muon::k_apply(int)", 10.0),
+                   ("muon::k_apply(int)", 30.0)])
+    w = _counters(tmp_path / "w.csv", "WRITE_SIZE",
+                  [(copy, 4 * 1024 * 1024.0), (copy, 5.0), ("muon::k_apply(int)", 40.0)])
+    text = profiling.traffic_summary(f, w, "t", "cmd")
+    assert "factors are 2.000 (fetch) and 1.000 (write)" in text
+    data = json.loads(text.split("```json\n")[1].split("\n```")[0])
+    assert data["traffic_bytes_per_launch"]["apply"] == round((20.0 * 2 + 40.0) * 1024)
