@@ -31,6 +31,8 @@
 //     rows of one cycle have distinct fsw >> 1, i.e. distinct 32-byte spans.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "muon_device.h"
 
 namespace muon {
@@ -377,10 +379,20 @@ __global__ __launch_bounds__(kFThreads) void k_ns_fused(const MatDesc* __restric
 template <int M>
 int launch_m(const MatDesc* d, int n, const float* coeffs, int n_coeffs, int ns_steps,
              int lds_bytes, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_ns_fused<M>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kFusedLdsMax);
-  if (attr != hipSuccess) return static_cast<int>(attr);
+  // the dynamic-LDS limit is raised once per device (the kernel needs up to
+  // 160 KB); later calls on that device skip it
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> done[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  if (!done[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ns_fused<M>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsMax);
+    if (e != hipSuccess) return static_cast<int>(e);
+    done[dev].store(true, std::memory_order_release);
+  }
   hipLaunchKernelGGL(k_ns_fused<M>, dim3(static_cast<unsigned>(n)), dim3(kFThreads),
                      static_cast<unsigned>(lds_bytes), stream, d, coeffs, n_coeffs, ns_steps);
   return static_cast<int>(hipGetLastError());

@@ -5,9 +5,10 @@
 
 The traffic summary records, per libmuon kernel, FETCH_SIZE and WRITE_SIZE
 (KiB per dispatch) scaled by what the same counters read for a plain device
-copy of known size in the same run, and stamps the result with a hash of the
-kernel sources.  bench.py reports a kernel's traffic only while that hash
-still matches the sources (a changed kernel makes the figure stale: null).
+copy of known size in the same run, and stamps each kernel's figure with a
+hash of the sources that kernel is built from.  bench.py reports a kernel's
+traffic only while that hash still matches the sources (a changed kernel
+makes its figure stale: null).
 """
 from __future__ import annotations
 
@@ -21,8 +22,14 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-KERNEL_SOURCES = ("muon_device.h", "muon_internal.h", "muon_kernels.hip", "muon_gemm.h",
-                  "muon_gemm256.hip", "muon_gemm128.hip", "muon_fused.hip")
+_COMMON = ("muon_device.h", "muon_internal.h")
+_ELEMENTWISE = _COMMON + ("muon_kernels.hip",)
+_GEMM = _COMMON + ("muon_gemm.h", "muon_gemm256.hip", "muon_gemm128.hip")
+# the sources each bench phase's kernel is compiled from
+SOURCES_OF = {"momentum_norm": _ELEMENTWISE, "normalize_cast": _ELEMENTWISE, "apply": _ELEMENTWISE,
+              "adamw": _ELEMENTWISE, "gram": _GEMM, "gram2_epilogue": _GEMM, "x_update": _GEMM,
+              "ns_fused": _COMMON + ("muon_fused.hip",)}
+KERNEL_SOURCES = tuple(sorted({f for files in SOURCES_OF.values() for f in files}))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "muon_step_transformer_d4096_hbm_traffic.md")
 
 # kernel symbol -> bench phase name
@@ -31,9 +38,10 @@ PHASE_OF = {"k_momentum_norm": "momentum_norm", "k_normalize": "normalize_cast",
             "k_xupdate<256>": "x_update", "k_apply": "apply"}
 
 
-def kernel_sources_hash() -> str:
+def kernel_sources_hash(phase: str | None = None) -> str:
+    """sha256[:16] over the sources of `phase` (all kernel sources if None)."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in (SOURCES_OF[phase] if phase else KERNEL_SOURCES):
         with open(os.path.join(PKG, "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -87,7 +95,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, title: str, commands: str,
             out.append(f"| `{sym}` | {fetch[sym]:.4g} | {write[sym]:.4g} | {b:.4g} |")
     out += ["", "Machine-readable (bench.py reports a kernel's traffic only while the hash matches "
             "the kernel sources):", "", "```json",
-            json.dumps({"kernel_sources_sha256_16": kernel_sources_hash(),
+            json.dumps({"kernel_sources_sha256_16": {k: kernel_sources_hash(k) for k in traffic},
                         "traffic_bytes_per_launch": {k: round(v) for k, v in traffic.items()}}),
             "```"]
     return "\n".join(out) + "\n"
@@ -104,10 +112,14 @@ def current_traffic(phase: str):
     if not m:
         return None
     data = json.loads(m.group(1))
-    if data.get("kernel_sources_sha256_16") != kernel_sources_hash():
-        return None
     v = data.get("traffic_bytes_per_launch", {}).get(phase)
-    return float(v) if v is not None else None
+    if v is None or phase not in SOURCES_OF:
+        return None
+    stamp = data.get("kernel_sources_sha256_16")
+    # per-kernel stamps; a single string stamps every kernel with all sources
+    want = stamp.get(phase) if isinstance(stamp, dict) else stamp
+    have = kernel_sources_hash(phase) if isinstance(stamp, dict) else kernel_sources_hash()
+    return float(v) if want == have else None
 
 
 if __name__ == "__main__":

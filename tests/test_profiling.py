@@ -6,10 +6,10 @@ import json
 from matrix_aware_optimizer_libmuon_amd import profiling
 
 
-def _profile(tmp_path, digest, value):
+def _profile(tmp_path, digest, value, phase="x_update"):
     p = tmp_path / "traffic.md"
     p.write_text("# t\n\n```json\n" + json.dumps(
-        {"kernel_sources_sha256_16": digest, "traffic_bytes_per_launch": {"x_update": value}}) + "\n```\n")
+        {"kernel_sources_sha256_16": digest, "traffic_bytes_per_launch": {phase: value}}) + "\n```\n")
     return str(p)
 
 
@@ -51,3 +51,14 @@ def test_traffic_calibrates_on_the_largest_copy(tmp_path):
     assert "factors are 2.000 (fetch) and 1.000 (write)" in text
     data = json.loads(text.split("```json\n")[1].split("\n```")[0])
     assert data["traffic_bytes_per_launch"]["apply"] == round((20.0 * 2 + 40.0) * 1024)
+
+
+def test_per_kernel_stamps(tmp_path, monkeypatch):
+    # a kernel's figure survives changes to sources it is not built from
+    stamps = {"x_update": profiling.kernel_sources_hash("x_update")}
+    monkeypatch.setattr(profiling, "TRAFFIC_PROFILE", _profile(tmp_path, stamps, 7))
+    assert profiling.current_traffic("x_update") == 7.0
+    assert "muon_fused.hip" not in profiling.SOURCES_OF["x_update"]
+    assert "muon_gemm.h" in profiling.SOURCES_OF["x_update"]
+    monkeypatch.setattr(profiling, "TRAFFIC_PROFILE", _profile(tmp_path, {"x_update": "0" * 16}, 7))
+    assert profiling.current_traffic("x_update") is None
