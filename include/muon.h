@@ -44,6 +44,11 @@
  *
  * Thread safety: calls may come from several host threads; two calls that
  * run concurrently must use different workspaces.
+ *
+ * Graph capture: every call stages its descriptor table through a small ring
+ * of pinned host buffers that later calls reuse, so a captured copy would
+ * replay stale tables.  A call on a stream that is capturing returns
+ * MUON_ECAPTURE before anything is launched.
  */
 #ifndef LIBMUON_MUON_H
 #define LIBMUON_MUON_H
@@ -62,6 +67,7 @@ extern "C" {
 #define MUON_EWORKSPACE -2   /* workspace missing, too small or misaligned    */
 #define MUON_EHIP       -3   /* a HIP runtime call or kernel launch failed    */
 #define MUON_EALIAS     -4   /* param / grad / momentum ranges overlap        */
+#define MUON_ECAPTURE   -5   /* the stream is capturing a graph (see below)    */
 
 /* ---- element types ----------------------------------------------------- */
 #define MUON_F32  0

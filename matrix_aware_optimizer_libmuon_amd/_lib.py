@@ -17,6 +17,7 @@ MUON_EINVAL = -1
 MUON_EWORKSPACE = -2
 MUON_EHIP = -3
 MUON_EALIAS = -4
+MUON_ECAPTURE = -5
 
 MUON_F32 = 0
 MUON_BF16 = 1

@@ -182,6 +182,12 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  // the staging ring is reused by later calls: a captured copy would replay
+  // whatever the slot holds then
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) return MUON_ECAPTURE;
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   Slot& s = st.slots[st.next];
@@ -724,6 +730,9 @@ const char* muon_status_string(int status) {
     case MUON_EINVAL: return "invalid argument";
     case MUON_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case MUON_EALIAS: return "param / grad / momentum (or in / out) ranges overlap";
+    case MUON_ECAPTURE:
+      return "the stream is capturing a graph: calls stage their descriptor table through "
+             "reused host buffers and cannot be captured";
     case MUON_EHIP:
       s = "HIP error: " + g_hip_detail;
       return s.c_str();

@@ -226,3 +226,30 @@ def test_checkpoint_resume_equals_straight_run():
     c.step(**kw)
     for i in range(2):
         assert rel(c.param(i), a.param(i)) <= 1e-7 and rel(c.mom(i), a.mom(i)) <= 1e-7
+
+
+def test_graph_capture_is_refused_before_anything_runs():
+    """A call on a capturing stream returns MUON_ECAPTURE and leaves the
+    parameters alone (the graph is ended, never replayed)."""
+    mi = W.adhoc_inputs(64, 96, "bf16", seed=60)
+    p = torch.from_numpy(mi.param).to(DEV)
+    m = torch.from_numpy(mi.mom).to(DEV)
+    g = torch.from_numpy(mi.grad_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    ws = muon.alloc_workspace([(64, 96)], DEV)
+    x = torch.zeros(4, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    err = None
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        try:
+            x.add_(1.0)                      # something to capture besides the refused call
+            muon.muon_step([p], [g], [m], workspace=ws)
+        except muon.LibMuonError as e:
+            err = e
+        finally:
+            graph.capture_end()
+    torch.cuda.synchronize()
+    assert err is not None and err.status == muon.MUON_ECAPTURE
+    assert np.array_equal(p.cpu().numpy(), mi.param) and np.array_equal(m.cpu().numpy(), mi.mom)

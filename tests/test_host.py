@@ -156,8 +156,10 @@ def test_orthogonalize_argument_errors(lib):
 
 
 def test_status_strings(lib):
-    for st in (muon.MUON_OK, muon.MUON_EINVAL, muon.MUON_EWORKSPACE, muon.MUON_EALIAS, muon.MUON_EHIP, -99):
+    for st in (muon.MUON_OK, muon.MUON_EINVAL, muon.MUON_EWORKSPACE, muon.MUON_EALIAS, muon.MUON_EHIP,
+               muon.MUON_ECAPTURE, -99):
         assert isinstance(muon.status_string(st), str) and muon.status_string(st)
+    assert "captur" in muon.status_string(muon.MUON_ECAPTURE)
     with pytest.raises(muon.LibMuonError):
         _lib.check(muon.MUON_EINVAL, "x")
 
