@@ -48,7 +48,8 @@
  * Graph capture: every call stages its descriptor table through a small ring
  * of pinned host buffers that later calls reuse, so a captured copy would
  * replay stale tables.  A call on a stream that is capturing returns
- * MUON_ECAPTURE before anything is launched.
+ * MUON_ECAPTURE before anything is launched; muon_plan_step (below) is the
+ * capturable form of a step.
  */
 #ifndef LIBMUON_MUON_H
 #define LIBMUON_MUON_H
@@ -173,6 +174,35 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats,
                  const muon_ns_coeff_t* coeffs, int n_coeffs,
                  int rms_scale_mode, float eps, const muon_options_t* options,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- a step prepared once over fixed buffers ----------------------------
+ * The pages' optimizer steps the same parameters every iteration (the
+ * Muon.step loop of airosetta.com; _step_muon of wmrh.cn section 4.2).  A plan
+ * fixes that list once: validation, the workspace plan and the descriptor
+ * table (with the coefficients) happen in muon_plan_create, which uploads the
+ * table into the workspace and waits for that copy.  muon_plan_step then only
+ * launches kernels: no host staging, no allocation, no synchronisation, so it
+ * may be captured into a HIP graph and replayed.
+ *   muon_plan_create  arguments as muon_step_ex (same errors, found before
+ *       anything is launched); *plan receives a host object the caller frees
+ *       with muon_plan_destroy.  The param, grad and momentum pointers and the
+ *       workspace are recorded: they must stay valid, and the workspace must
+ *       not be used by other calls, while the plan lives.  New gradients are
+ *       written into the same grad buffers.
+ *   muon_plan_step    one step of the plan on `stream`, on the device the plan
+ *       was created on (else MUON_EINVAL).  `hyper` points to three floats in
+ *       device memory, {lr, mu, wd}, read by the kernels when they run, so a
+ *       schedule updates them between replays.
+ * Each step clears the workspace's norm slots with a fill kernel (no
+ * memset), so replays do not depend on the previous step's workspace.  Phase
+ * timing (muon_timing_enable) is skipped while the stream is capturing. */
+typedef struct muon_plan muon_plan_t;
+int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
+                     const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
+                     const muon_options_t* options, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, muon_plan_t** plan);
+int muon_plan_step(const muon_plan_t* plan, const float* hyper, hipStream_t stream);
+void muon_plan_destroy(muon_plan_t* plan);
 
 /* Orthogonalisation alone: out = NS(in) with the same normalisation,
  * short-side rule and bf16 iteration as muon_step, for a list of matrices.

@@ -152,6 +152,70 @@ def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 
     return workspace
 
 
+class Plan:
+    """A Muon step prepared once over fixed tensors (``muon_plan_create``):
+    ``step()`` then only launches kernels, so it can be captured into a CUDA
+    (HIP) graph and replayed.  Write new gradients into the same grad tensors
+    between steps; ``lr``, ``mu`` and ``wd`` live in the device tensor
+    ``hyper`` ({lr, mu, wd}, float32), read by the kernels when they run, so
+    ``set_hyper`` follows a schedule across replays.  The tensors and the
+    workspace are kept alive by the plan."""
+
+    def __init__(self, params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 0.02,
+                 mu: float = 0.95, wd: float = 0.0, ns_steps: int = 5, coeffs=QUINTIC,
+                 rms_scale: str | None = None, eps: float = 1e-7, scales: Sequence | None = None,
+                 zero_centering: bool = False, nesterov: bool = False, ns_first: bool = False,
+                 workspace=None, stream=None):
+        torch = _torch()
+        n = len(params)
+        if rms_scale not in (None, "none", "sqrt_max1"):
+            raise ValueError(f"unknown rms_scale {rms_scale!r}")
+        mode = MUON_SCALE_SQRT_MAX1 if rms_scale == "sqrt_max1" else MUON_SCALE_NONE
+        arr = (MuonMatrix * max(1, n))()
+        sc = [] if scales is None else [0.0 if s is None else float(s) for s in scales]
+        _marshaller().fill_matrices(params, grads, moms, sc, ctypes.addressof(arr))
+        self.device = params[0].device if n else torch.device("cuda")
+        self.tensors = (list(params), list(grads), list(moms))
+        if workspace is None:
+            workspace = alloc_workspace([tuple(p.shape) for p in params], self.device)
+        self.workspace = workspace
+        self.hyper = torch.tensor([lr, mu, wd], dtype=torch.float32, device=self.device)
+        flags = ((MUON_OPT_ZERO_CENTER if zero_centering else 0)
+                 | (MUON_OPT_NESTEROV if nesterov else 0) | (MUON_OPT_NS_FIRST if ns_first else 0))
+        opts = MuonOptions(flags, 0)
+        carr, nc = _coeff_array(coeffs, ns_steps)
+        self._lib = _lib.load()
+        handle = ctypes.c_void_p()
+        st = self._lib.muon_plan_create(arr, n, int(ns_steps), carr, nc, mode, float(eps),
+                                        ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream, self.device), ctypes.byref(handle))
+        _lib.check(st, "muon_plan_create")
+        self._handle = handle
+
+    def set_hyper(self, lr: float | None = None, mu: float | None = None,
+                  wd: float | None = None) -> None:
+        """Stream-ordered update of {lr, mu, wd} on the device."""
+        for k, v in enumerate((lr, mu, wd)):
+            if v is not None:
+                self.hyper[k] = float(v)
+
+    def step(self, stream=None) -> None:
+        if not self._handle:
+            raise RuntimeError("plan is closed")
+        _lib.check(self._lib.muon_plan_step(self._handle, ctypes.c_void_p(self.hyper.data_ptr()),
+                                            _stream_handle(stream, self.device)),
+                   "muon_plan_step")
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            self._lib.muon_plan_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        self.close()
+
+
 def orthogonalize(inputs: Sequence, outputs: Sequence | None = None, *, ns_steps: int = 5,
                   coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None):
     """out_i = NS(in_i) in bf16 for a list of 2-D fp32/bf16 GPU tensors.

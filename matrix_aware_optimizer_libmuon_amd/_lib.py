@@ -33,7 +33,8 @@ MUON_PHASES = 8
 PHASE_NAMES = ("momentum_norm", "normalize_cast", "gram", "gram2_epilogue", "x_update", "apply",
                "adamw", "ns_fused")
 
-EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_step_ex", "muon_orthogonalize",
+EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_step_ex", "muon_plan_create",
+            "muon_plan_step", "muon_plan_destroy", "muon_orthogonalize",
             "muon_workspace_view",
             "muon_adamw_workspace_bytes", "muon_adamw_step",
             "muon_timing_enable", "muon_timing_read", "muon_status_string", "muon_version")
@@ -104,6 +105,15 @@ def load() -> ctypes.CDLL:
                                  ctypes.c_int, ctypes.c_float, P(MuonOptions), ctypes.c_void_p,
                                  ctypes.c_size_t, ctypes.c_void_p]
     lib.muon_step_ex.restype = ctypes.c_int
+    lib.muon_plan_create.argtypes = [P(MuonMatrix), ctypes.c_int64, ctypes.c_int, P(MuonCoeff),
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, P(MuonOptions),
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     P(ctypes.c_void_p)]
+    lib.muon_plan_create.restype = ctypes.c_int
+    lib.muon_plan_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.muon_plan_step.restype = ctypes.c_int
+    lib.muon_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.muon_plan_destroy.restype = None
     lib.muon_orthogonalize.argtypes = [P(MuonOrtho), ctypes.c_int64, ctypes.c_int, P(MuonCoeff),
                                        ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]

@@ -8,8 +8,10 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "muon.h"
@@ -145,8 +147,10 @@ struct Slot {
   bool pending = false;
 };
 
+constexpr int kSlots = 8;
+
 struct DeviceState {
-  Slot slots[4];
+  Slot slots[kSlots];
   int next = 0;
 };
 
@@ -159,6 +163,7 @@ struct TimingRec {
   hipEvent_t a, b;
 };
 bool g_timing = false;
+thread_local bool g_no_timing = false;   // set while launching into a capturing stream
 std::vector<TimingRec> g_trecs;
 std::vector<hipEvent_t> g_evpool;
 
@@ -191,10 +196,13 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   Slot& s = st.slots[st.next];
-  st.next = (st.next + 1) % 4;
+  st.next = (st.next + 1) % kSlots;
   if (s.pending) {
-    e = hipEventSynchronize(s.ev);  // the copy that last used this slot has finished
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
+    // wait for the copy that last used this slot: polled, since a blocking
+    // wait sleeps in steps of about a millisecond, far longer than a whole
+    // step over a few small matrices
+    while ((e = hipEventQuery(s.ev)) == hipErrorNotReady) std::this_thread::yield();
+    if (e != hipSuccess) return hip_fail(e, "hipEventQuery (staging)");
     s.pending = false;
   }
   if (!s.ev) {
@@ -228,7 +236,7 @@ int timed(int phase, hipStream_t stream, F&& launch) {
   bool timing;
   {
     std::lock_guard<std::mutex> lock(g_mu);
-    timing = g_timing;
+    timing = g_timing && !g_no_timing;
     if (timing) {
       a = pool_event();
       b = pool_event();
@@ -372,18 +380,23 @@ void build_table(const Plan& plan, char* ws, int n_active, Fill fill, Table& t) 
   for (int k = 0; k < kNumPrefix; ++k) t.units[k] = acc[k];
 }
 
-int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, float mu,
-                 float wd, int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, float eps,
-                 hipStream_t stream) {
-  // the coefficients travel with the table (the fused kernel reads them)
+// The coefficients travel with the table (the fused kernel reads them).
+void fill_coeffs(const Plan& plan, Table& t, int ns_steps, const muon_ns_coeff_t* coeffs,
+                 int n_coeffs) {
   float* cf = reinterpret_cast<float*>(t.bytes.data() + plan.coeff_off);
   for (int k = 0; k < (ns_steps > 0 ? n_coeffs : 0); ++k) {
     cf[3 * k] = coeffs[k].a;
     cf[3 * k + 1] = coeffs[k].b;
     cf[3 * k + 2] = coeffs[k].c;
   }
-  int rc = upload_table(t.bytes.data(), t.bytes.size(), ws, stream);
-  if (rc != MUON_OK) return rc;
+}
+
+// Every launch of one step over a table already in the workspace.  `hyper`
+// (device {lr, mu, wd}) overrides the scalar arguments when not null.
+int launch_all(const Plan& plan, const Table& t, char* ws, bool ortho, float lr, float mu,
+               float wd, const float* hyper, int ns_steps, const muon_ns_coeff_t* coeffs,
+               int n_coeffs, float eps, hipStream_t stream) {
+  int rc = MUON_OK;
   if (t.n_active == 0) return MUON_OK;
   const MatDesc* d = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
   const int64_t* pre[kNumPrefix];
@@ -401,11 +414,11 @@ int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, flo
     if (rc) return rc;
   }
   rc = timed(kPhaseMomentumNorm, stream, [&] {
-    return launch_momentum_norm(d, pre[kPreFlat], n, t.units[kPreFlat], mu, ortho ? 1 : 0, s);
+    return launch_momentum_norm(d, pre[kPreFlat], n, t.units[kPreFlat], mu, hyper, ortho ? 1 : 0, s);
   });
   if (rc) return rc;
   rc = timed(kPhaseNormalize, stream, [&] {
-    return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, mu, s);
+    return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, mu, hyper, s);
   });
   if (rc) return rc;
   const MatDesc* df = d_fused;
@@ -446,27 +459,29 @@ int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, flo
     if (rc) return rc;
   }
   rc = timed(kPhaseApply, stream, [&] {
-    return launch_apply(d, pre[kPreRows], n, t.units[kPreRows], ns_steps & 1, lr, wd, mu, ortho ? 1 : 0, s);
+    return launch_apply(d, pre[kPreRows], n, t.units[kPreRows], ns_steps & 1, lr, wd, mu, hyper,
+                        ortho ? 1 : 0, s);
   });
   return rc;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n_mats) {
-  if (n_mats <= 0 || !mats) return 0;
-  Plan plan;
-  if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
-    return 0;
-  return plan.total;
+int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, float mu,
+                 float wd, int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, float eps,
+                 hipStream_t stream) {
+  fill_coeffs(plan, t, ns_steps, coeffs, n_coeffs);
+  int rc = upload_table(t.bytes.data(), t.bytes.size(), ws, stream);
+  if (rc != MUON_OK) return rc;
+  return launch_all(plan, t, ws, ortho, lr, mu, wd, nullptr, ns_steps, coeffs, n_coeffs, eps,
+                    stream);
 }
 
-int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd,
+// Validation and descriptor table of a step (muon_step_ex and muon_plan_create).
+// Returns MUON_OK with t.n_active == 0 when there is nothing to launch.
+int prepare_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd,
                  int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode,
-                 float eps, const muon_options_t* options, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+                 float eps, const muon_options_t* options, void* workspace,
+                 size_t workspace_bytes, Plan& plan, Table& t) {
+  t = Table();
   uint32_t variant = 0;
   if (options) {
     const uint32_t known = MUON_OPT_ZERO_CENTER | MUON_OPT_NESTEROV | MUON_OPT_NS_FIRST;
@@ -502,13 +517,11 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
     ++n_active;
   }
   if (any_overlap(ranges)) return MUON_EALIAS;
-  Plan plan;
   if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
     return MUON_EINVAL;
   if (!workspace || workspace_bytes < plan.total || !aligned(workspace, kAlign)) return MUON_EWORKSPACE;
   if (n_active == 0) return MUON_OK;
   char* ws = static_cast<char*>(workspace);
-  Table t;
   build_table(plan, ws, n_active, [&](size_t i, MatDesc& d) {
     const muon_matrix_t& m = mats[i];
     if (!m.grad) return false;
@@ -528,7 +541,44 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
     else d.scale = 1.0f;
     return true;
   }, t);
-  return run_sequence(plan, t, ws, false, lr, mu, wd, ns_steps, coeffs, n_coeffs, eps, stream);
+  return MUON_OK;
+}
+
+}  // namespace
+
+// A step prepared once over fixed buffers (muon_plan_create).
+struct muon_plan {
+  Plan plan;
+  Table t;
+  char* ws = nullptr;
+  int device = 0;
+  int ns_steps = 0;
+  int n_coeffs = 0;
+  float eps = 0.f;
+  std::vector<muon_ns_coeff_t> coeffs;
+};
+
+extern "C" {
+
+size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n_mats) {
+  if (n_mats <= 0 || !mats) return 0;
+  Plan plan;
+  if (!make_plan(n_mats, [&](int64_t i, int64_t& r, int64_t& c) { r = mats[i].rows; c = mats[i].cols; }, plan))
+    return 0;
+  return plan.total;
+}
+
+int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd,
+                 int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode,
+                 float eps, const muon_options_t* options, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  Plan plan;
+  Table t;
+  const int rc = prepare_step(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs,
+                              rms_scale_mode, eps, options, workspace, workspace_bytes, plan, t);
+  if (rc != MUON_OK || t.n_active == 0) return rc;
+  return run_sequence(plan, t, static_cast<char*>(workspace), false, lr, mu, wd, ns_steps, coeffs,
+                      n_coeffs, eps, stream);
 }
 
 int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd, int ns_steps,
@@ -537,6 +587,62 @@ int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, flo
   return muon_step_ex(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs, rms_scale_mode, eps,
                       nullptr, workspace, workspace_bytes, stream);
 }
+
+int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
+                     const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
+                     const muon_options_t* options, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, muon_plan_t** out) {
+  if (!out) return MUON_EINVAL;
+  *out = nullptr;
+  std::unique_ptr<muon_plan> p(new (std::nothrow) muon_plan());
+  if (!p) return MUON_EINVAL;
+  int rc = prepare_step(mats, n_mats, 0.f, 0.f, 0.f, ns_steps, coeffs, n_coeffs, rms_scale_mode,
+                        eps, options, workspace, workspace_bytes, p->plan, p->t);
+  if (rc != MUON_OK) return rc;
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  p->ws = static_cast<char*>(workspace);
+  p->ns_steps = ns_steps;
+  p->n_coeffs = n_coeffs;
+  p->eps = eps;
+  if (ns_steps > 0) p->coeffs.assign(coeffs, coeffs + n_coeffs);
+  if (p->t.n_active > 0) {
+    fill_coeffs(p->plan, p->t, ns_steps, coeffs, n_coeffs);
+    rc = upload_table(p->t.bytes.data(), p->t.bytes.size(), p->ws, stream);
+    if (rc != MUON_OK) return rc;
+    e = hipStreamSynchronize(stream);  // the table is in place before the plan is used
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (plan table)");
+  }
+  *out = p.release();
+  return MUON_OK;
+}
+
+int muon_plan_step(const muon_plan_t* plan, const float* hyper, hipStream_t stream) {
+  if (!plan || !hyper || !aligned(hyper, 4)) return MUON_EINVAL;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device) return MUON_EINVAL;
+  if (plan->t.n_active == 0) return MUON_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  // events recorded inside a graph cannot be read back: no phase timing then
+  g_no_timing = cap != hipStreamCaptureStatusNone;
+  char* ws = plan->ws;
+  int rc = timed(kPhaseMomentumNorm, stream, [&] {
+    return launch_fill_zero(reinterpret_cast<double*>(ws + plan->plan.nrm2_off), plan->plan.n,
+                            static_cast<void*>(stream));
+  });
+  if (rc == MUON_OK)
+    rc = launch_all(plan->plan, plan->t, ws, false, 0.f, 0.f, 0.f, hyper, plan->ns_steps,
+                    plan->coeffs.empty() ? nullptr : plan->coeffs.data(), plan->n_coeffs, plan->eps,
+                    stream);
+  g_no_timing = false;
+  return rc;
+}
+
+void muon_plan_destroy(muon_plan_t* plan) { delete plan; }
 
 int muon_orthogonalize(const muon_ortho_t* mats, int64_t n_mats, int ns_steps,
                        const muon_ns_coeff_t* coeffs, int n_coeffs, float eps, void* workspace,

@@ -104,11 +104,14 @@ struct alignas(16) AdamDesc {
 };
 static_assert(sizeof(AdamDesc) == 64, "AdamW descriptor size");
 
-// kernel launchers (muon_kernels.hip); return hipError_t as int
+// kernel launchers (muon_kernels.hip); return hipError_t as int.  `hyper`,
+// when not null, points to {lr, mu, wd} in device memory and replaces the
+// scalar arguments (read by the kernels when they run).
 int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
-                         float mu, int norm_only, void* stream);
+                         float mu, const float* hyper, int norm_only, void* stream);
 int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
-                     float eps, float mu, void* stream);
+                     float eps, float mu, const float* hyper, void* stream);
+int launch_fill_zero(double* p, int64_t count, void* stream);
 int launch_colsum(const MatDesc* d, const int64_t* prefix, int n, int64_t units, double* zero_from,
                   int64_t zero_count, void* stream);
 // GEMM phases: `tile` is 128 or 256; every matrix of the launch is of that class
@@ -119,7 +122,7 @@ int launch_gram2(int tile, const MatDesc* d, const int64_t* prefix, int n, int64
 int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                    int parity, void* stream);
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                 float lr, float wd, float mu, int export_only, void* stream);
+                 float lr, float wd, float mu, const float* hyper, int export_only, void* stream);
 int launch_adamw(const AdamDesc* d, const int64_t* prefix, int n, int64_t units, float beta1,
                  float beta2, float eps, void* stream);
 // fused iteration (muon_fused.hip): one workgroup per descriptor d[0 .. n),

@@ -86,8 +86,12 @@ __device__ __forceinline__ float k1_elem(float& m, float g, float mu, float omu,
 
 __global__ __launch_bounds__(kEwThreads) void k_momentum_norm(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n,
-    float mu, float omu, int norm_only) {
+    float mu, float omu, const float* __restrict__ hyper, int norm_only) {
   __shared__ double red[4];
+  if (hyper) {
+    mu = gld<float>(hyper + 1);
+    omu = 1.0f - mu;
+  }
   const int64_t unit = blockIdx.x;
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
@@ -247,7 +251,8 @@ struct RowWalk {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kEwThreads) void k_normalize(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, float eps,
-    float mu) {
+    float mu, const float* __restrict__ hyper) {
+  if (hyper) mu = gld<float>(hyper + 1);
   const int64_t unit = blockIdx.x;
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
@@ -314,7 +319,12 @@ __global__ __launch_bounds__(kEwThreads) void k_normalize(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kEwThreads) void k_apply(
     const MatDesc* __restrict__ descs, const int64_t* __restrict__ prefix, int n, int parity,
-    float lr, float wd, float mu, int export_only) {
+    float lr, float wd, float mu, const float* __restrict__ hyper, int export_only) {
+  if (hyper) {
+    lr = gld<float>(hyper);
+    mu = gld<float>(hyper + 1);
+    wd = gld<float>(hyper + 2);
+  }
   const int64_t unit = blockIdx.x;
   const int i = find_matrix(prefix, n, unit);
   const MatDesc& d = descs[i];
@@ -449,18 +459,26 @@ __global__ __launch_bounds__(kEwThreads) void k_adamw(const AdamDesc* __restrict
 static inline int grid_ok(int64_t units) { return units > 0 && units < (int64_t(1) << 31); }
 
 int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float mu,
-                         int norm_only, void* stream) {
+                         const float* hyper, int norm_only, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_momentum_norm, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, mu, 1.0f - mu, norm_only);
+                     static_cast<hipStream_t>(stream), d, prefix, n, mu, 1.0f - mu, hyper, norm_only);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units, float eps,
-                     float mu, void* stream) {
+                     float mu, const float* hyper, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_normalize, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, eps, mu);
+                     static_cast<hipStream_t>(stream), d, prefix, n, eps, mu, hyper);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_fill_zero(double* p, int64_t count, void* stream) {
+  if (count <= 0) return 0;
+  const int64_t blocks = (count + kEwThreads - 1) / kEwThreads;
+  hipLaunchKernelGGL(k_fill_zero_f64, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)),
+                     dim3(kEwThreads), 0, static_cast<hipStream_t>(stream), p, count);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -499,10 +517,11 @@ int launch_xupdate(int tile, const MatDesc* d, const int64_t* prefix, int n, int
 }
 
 int launch_apply(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
-                 float lr, float wd, float mu, int export_only, void* stream) {
+                 float lr, float wd, float mu, const float* hyper, int export_only, void* stream) {
   if (!grid_ok(units)) return static_cast<int>(hipErrorInvalidConfiguration);
   hipLaunchKernelGGL(k_apply, dim3(static_cast<unsigned>(units)), dim3(kEwThreads), 0,
-                     static_cast<hipStream_t>(stream), d, prefix, n, parity, lr, wd, mu, export_only);
+                     static_cast<hipStream_t>(stream), d, prefix, n, parity, lr, wd, mu, hyper,
+                     export_only);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -290,3 +290,23 @@ def test_kernel_class_by_shape(lib):
     assert tile(1024, 1024) == 256 and tile(4096, 14336) == 256
     v = muon.workspace_view([(100, 300)], 0, 5)
     assert (v["rows_pad"], v["cols_pad"], v["m_pad"]) == (128, 320, 128)
+
+
+def test_plan_arguments_are_validated_on_the_host(lib):
+    ok = _mats([GOOD])
+    c = (muon.MuonCoeff * 1)(muon.MuonCoeff(3.4445, -4.775, 2.0315))
+    out = ctypes.c_void_p()
+
+    def create(arr, n, *, ns=5, ws_bytes=1 << 60, out_ptr=True, opts=None):
+        return lib.muon_plan_create(arr, n, ns, c, 1, 0, 1e-7, opts, ctypes.c_void_p(1 << 40), ws_bytes,
+                                    None, ctypes.byref(out) if out_ptr else None)
+
+    assert create(ok, 1, out_ptr=False) == muon.MUON_EINVAL
+    assert create(ok, 1, ns=-1) == muon.MUON_EINVAL
+    assert create(ok, 1, ws_bytes=16) == muon.MUON_EWORKSPACE
+    assert create(_mats([dict(GOOD, momentum=GOOD["param"] + 64)]), 1) == muon.MUON_EALIAS
+    bad = muon.MuonOptions(muon.MUON_OPT_NESTEROV | muon.MUON_OPT_NS_FIRST, 0)
+    assert create(ok, 1, opts=ctypes.byref(bad)) == muon.MUON_EINVAL
+    assert out.value is None                         # nothing was created
+    assert lib.muon_plan_step(None, ctypes.c_void_p(1 << 40), None) == muon.MUON_EINVAL
+    lib.muon_plan_destroy(None)                      # a no-op
