@@ -198,9 +198,8 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   Slot& s = st.slots[st.next];
   st.next = (st.next + 1) % kSlots;
   if (s.pending) {
-    // wait for the copy that last used this slot: polled, since a blocking
-    // wait sleeps in steps of about a millisecond, far longer than a whole
-    // step over a few small matrices
+    // wait for the copy that last used this slot (polled: a blocking wait
+    // may put the thread to sleep for longer than a small step takes)
     while ((e = hipEventQuery(s.ev)) == hipErrorNotReady) std::this_thread::yield();
     if (e != hipSuccess) return hip_fail(e, "hipEventQuery (staging)");
     s.pending = false;
