@@ -5,7 +5,12 @@
  * All device memory (parameters, gradients, momentum buffers, outputs and the
  * workspace) is owned by the caller.  The library launches work on the
  * caller's HIP stream and never waits for it, except where a function below
- * says so.
+ * says so.  A step whose matrices fall both into the fused class and into a
+ * tiled class (muon_step) also uses one stream of the library's own per
+ * device (a plan: its own), forked from the caller's stream with an event
+ * after the normalisation pass and joined back before the update pass: work
+ * queued on the caller's stream before the call still runs first, work queued
+ * after it still sees the finished step.
  *
  * What one step computes, for every 2-D matrix in the list (pages cited by
  * title and section):
@@ -195,7 +200,10 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats,
  *       schedule updates them between replays.
  * Each step clears the workspace's norm slots with a fill kernel (no
  * memset), so replays do not depend on the previous step's workspace.  Phase
- * timing (muon_timing_enable) is skipped while the stream is capturing. */
+ * timing (muon_timing_enable) is skipped while the stream is capturing.  A
+ * plan over both fused and tiled matrices owns a stream and two events
+ * (created here, released by muon_plan_destroy); a captured step forks onto
+ * that stream and joins back, so the graph holds two parallel branches. */
 typedef struct muon_plan muon_plan_t;
 int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
                      const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
@@ -296,7 +304,9 @@ int muon_adamw_step(const muon_adamw_tensor_t* tensors, int64_t n_tensors, float
                     hipStream_t stream);
 
 /* Phase timing with HIP events, for benchmarks.  When enabled, every launch
- * is bracketed by a pair of events on the call's stream.  muon_timing_read()
+ * is bracketed by a pair of events on the call's stream, and a step keeps
+ * all its launches on that stream (no side-stream overlap, so that each
+ * phase's events bracket its own kernels only).  muon_timing_read()
  * waits for the recorded events, returns the summed milliseconds and launch
  * counts per phase (MUON_PHASES entries each; either pointer may be NULL) and
  * clears the record.  Phases: momentum+norm, normalise+cast, Gram X X^T,

@@ -227,6 +227,66 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// side stream: the fused class runs beside the tiled GEMM launches
+// ---------------------------------------------------------------------------
+// A fork/join pair: a stream (default priority) and the two events that order
+// it after the caller's stream and the caller's stream after it again.  The
+// eager calls share one pair per device, created on first use and kept for the
+// process, and take g_mu around each record + wait so that concurrent callers
+// do not reuse an event between the two (a wait takes the event's state at the
+// time of the call).  A prepared plan owns a pair of its own, which also joins
+// a graph capture of its step.
+struct SidePair {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+  bool shared = false;  // the per-device pair: record + wait under g_mu
+};
+std::map<int, SidePair> g_side;
+
+int make_side(SidePair& sp) {
+  hipError_t e = hipStreamCreateWithFlags(&sp.stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&sp.fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&sp.join, hipEventDisableTiming);
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "side stream / events");
+}
+
+void free_side(SidePair& sp) {
+  if (sp.join) (void)hipEventDestroy(sp.join);
+  if (sp.fork) (void)hipEventDestroy(sp.fork);
+  if (sp.stream) (void)hipStreamDestroy(sp.stream);
+  sp = SidePair();
+}
+
+// The current device's shared pair.
+int shared_side(SidePair*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  SidePair& sp = g_side[dev];
+  if (!sp.stream) {
+    const int rc = make_side(sp);
+    if (rc) {
+      free_side(sp);
+      return rc;
+    }
+    sp.shared = true;
+  }
+  out = &sp;
+  return MUON_OK;
+}
+
+// `to` waits for everything queued on `from` so far, through `ev`.
+int stream_after(const SidePair& sp, hipEvent_t ev, hipStream_t to, hipStream_t from) {
+  std::unique_lock<std::mutex> lock(g_mu, std::defer_lock);
+  if (sp.shared) lock.lock();
+  hipError_t e = hipEventRecord(ev, from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "stream fork / join");
+}
+
+// ---------------------------------------------------------------------------
 // launch sequence
 // ---------------------------------------------------------------------------
 template <class F>
@@ -392,9 +452,14 @@ void fill_coeffs(const Plan& plan, Table& t, int ns_steps, const muon_ns_coeff_t
 
 // Every launch of one step over a table already in the workspace.  `hyper`
 // (device {lr, mu, wd}) overrides the scalar arguments when not null.
+// Both a fused class and a tiled class to run: the step forks.
+bool wants_side(const Table& t, int ns_steps) {
+  return ns_steps > 0 && t.n_fused > 0 && t.n_big + t.n_small > 0;
+}
+
 int launch_all(const Plan& plan, const Table& t, char* ws, bool ortho, float lr, float mu,
                float wd, const float* hyper, int ns_steps, const muon_ns_coeff_t* coeffs,
-               int n_coeffs, float eps, hipStream_t stream) {
+               int n_coeffs, float eps, hipStream_t stream, const SidePair* side) {
   int rc = MUON_OK;
   if (t.n_active == 0) return MUON_OK;
   const MatDesc* d = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
@@ -420,17 +485,38 @@ int launch_all(const Plan& plan, const Table& t, char* ws, bool ortho, float lr,
     return launch_normalize(d, pre[kPrePad], n, t.units[kPrePad], eps, mu, hyper, s);
   });
   if (rc) return rc;
+  // The fused class and the tiled classes are independent: when both are
+  // present the fused launches go to the side stream (forked after the
+  // normalisation, joined before the apply pass) and overlap the tiled ones.
+  // Phase timing keeps them on one stream, so that each phase's events
+  // bracket its own kernels only.
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    timing = g_timing && !g_no_timing;
+  }
+  const bool fork = side && !timing && nf > 0 && ns_steps > 0 && (nb + ns) > 0;
+  hipStream_t fs = fork ? side->stream : stream;
+  if (fork) {
+    rc = stream_after(*side, side->fork, fs, stream);
+    if (rc) return rc;
+  }
   const MatDesc* df = d_fused;
   for (int c = 0; c < 4 && nf > 0 && ns_steps > 0; ++c) {
     const int cnt = t.fused_n[c];
     if (cnt == 0) continue;
-    rc = timed(kPhaseFusedNS, stream, [&] {
+    rc = timed(kPhaseFusedNS, fs, [&] {
       return launch_ns_fused(kTileFused * (c + 1), df, cnt,
                              reinterpret_cast<const float*>(ws + plan.coeff_off), n_coeffs,
-                             ns_steps, t.fused_lds[c], s);
+                             ns_steps, t.fused_lds[c], static_cast<void*>(fs));
     });
-    if (rc) return rc;
+    if (rc) break;
     df += cnt;
+  }
+  if (rc) {
+    // rejoin even on failure, so that a capture is not left with a loose branch
+    if (fork) (void)stream_after(*side, side->join, stream, fs);
+    return rc;
   }
   for (int k = 0; k < ((nb + ns) > 0 ? ns_steps : 0); ++k) {
     const muon_ns_coeff_t& c = coeffs[n_coeffs == 1 ? 0 : k];
@@ -441,22 +527,27 @@ int launch_all(const Plan& plan, const Table& t, char* ws, bool ortho, float lr,
       if (!e && ns) e = launch_gram(kTileSmall, d_small, pre[kPreSymSmall], ns, t.units[kPreSymSmall], parity, s);
       return e;
     });
-    if (rc) return rc;
+    if (rc) break;
     rc = timed(kPhaseGram2, stream, [&] {
       int e = 0;
       if (nb) e = launch_gram2(kTileBig, d, pre[kPreSymBig], nb, t.units[kPreSymBig], c.a, c.b, c.c, s);
       if (!e && ns) e = launch_gram2(kTileSmall, d_small, pre[kPreSymSmall], ns, t.units[kPreSymSmall], c.a, c.b, c.c, s);
       return e;
     });
-    if (rc) return rc;
+    if (rc) break;
     rc = timed(kPhaseXUpdate, stream, [&] {
       int e = 0;
       if (nb) e = launch_xupdate(kTileBig, d, pre[kPreFullBig], nb, t.units[kPreFullBig], parity, s);
       if (!e && ns) e = launch_xupdate(kTileSmall, d_small, pre[kPreFullSmall], ns, t.units[kPreFullSmall], parity, s);
       return e;
     });
-    if (rc) return rc;
+    if (rc) break;
   }
+  if (fork) {
+    const int jrc = stream_after(*side, side->join, stream, fs);
+    if (!rc) rc = jrc;
+  }
+  if (rc) return rc;
   rc = timed(kPhaseApply, stream, [&] {
     return launch_apply(d, pre[kPreRows], n, t.units[kPreRows], ns_steps & 1, lr, wd, mu, hyper,
                         ortho ? 1 : 0, s);
@@ -470,8 +561,13 @@ int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, flo
   fill_coeffs(plan, t, ns_steps, coeffs, n_coeffs);
   int rc = upload_table(t.bytes.data(), t.bytes.size(), ws, stream);
   if (rc != MUON_OK) return rc;
+  SidePair* side = nullptr;
+  if (wants_side(t, ns_steps)) {
+    rc = shared_side(side);
+    if (rc != MUON_OK) return rc;
+  }
   return launch_all(plan, t, ws, ortho, lr, mu, wd, nullptr, ns_steps, coeffs, n_coeffs, eps,
-                    stream);
+                    stream, side);
 }
 
 // Validation and descriptor table of a step (muon_step_ex and muon_plan_create).
@@ -555,6 +651,8 @@ struct muon_plan {
   int n_coeffs = 0;
   float eps = 0.f;
   std::vector<muon_ns_coeff_t> coeffs;
+  SidePair side;  // own fork / join pair, when the step forks
+  ~muon_plan() { free_side(side); }
 };
 
 extern "C" {
@@ -605,6 +703,10 @@ int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
   p->n_coeffs = n_coeffs;
   p->eps = eps;
   if (ns_steps > 0) p->coeffs.assign(coeffs, coeffs + n_coeffs);
+  if (wants_side(p->t, ns_steps)) {
+    rc = make_side(p->side);
+    if (rc != MUON_OK) return rc;
+  }
   if (p->t.n_active > 0) {
     fill_coeffs(p->plan, p->t, ns_steps, coeffs, n_coeffs);
     rc = upload_table(p->t.bytes.data(), p->t.bytes.size(), p->ws, stream);
@@ -636,7 +738,7 @@ int muon_plan_step(const muon_plan_t* plan, const float* hyper, hipStream_t stre
   if (rc == MUON_OK)
     rc = launch_all(plan->plan, plan->t, ws, false, 0.f, 0.f, 0.f, hyper, plan->ns_steps,
                     plan->coeffs.empty() ? nullptr : plan->coeffs.data(), plan->n_coeffs, plan->eps,
-                    stream);
+                    stream, plan->side.stream ? &plan->side : nullptr);
   g_no_timing = false;
   return rc;
 }
