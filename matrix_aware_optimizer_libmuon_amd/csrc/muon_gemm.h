@@ -209,7 +209,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   slots 0 .. H-1:            A rows of pass 1 of this step (stage kt)
 //   slots H*NB .. H*NB+H-1:    A rows of pass 0 of step kt+1
 //   after each column of pass 1: that column's B fragment of step kt+1
-//   slots H, H + LSS, ...:     the loads of step kt+3
+//   slots H, H + LSS, ...:     the loads of step kt+3 (spread as LSS says)
 // The step opens with a wait for this wave's loads of step kt+1 and an LDS
 // barrier: step kt+1 is then visible, and every wave is past its reads of
 // step kt-1, so stage (kt+3) mod 4 is free.  Loads past the end re-read the
@@ -224,7 +224,11 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
   using G = Geo<TILE>;
   constexpr int NB = G::NB, H = NB / 2, PASS = H * NB, SLOTS = NB * NB;
   constexpr int LPS = 2 * G::LPW;                                // loads per wave per step
-  constexpr int LSS = (PASS - H) / LPS > 0 ? (PASS - H) / LPS : 1;
+  // load spacing: over the whole step at TILE 256 (the 32 loads per CU and
+  // step then never queue up behind each other and hold up the MFMA issue;
+  // 1-2 % on the large sets), within the first pass at TILE 128 (where
+  // spreading measured no better)
+  constexpr int LSS = TILE == 256 ? (SLOTS - H) / LPS : ((PASS - H) / LPS > 0 ? (PASS - H) / LPS : 1);
   static_assert(H + (LPS - 1) * LSS < SLOTS, "load slots exceed the step");
   const int w = threadIdx.x >> 6;
   const int rowA = G::WT * (w >> 1), rowB = G::WT * (w & 1);
@@ -581,7 +585,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
     const int r = idx / CPR, ch = idx % CPR;
     const u32x2 lo = *reinterpret_cast<const u32x2*>(smem + r * TILE + (((2 * ch) ^ (r & 31)) << 2));
     const u32x2 hi = *reinterpret_cast<const u32x2*>(smem + r * TILE + (((2 * ch + 1) ^ (r & 31)) << 2));
-    gst<u32x4>(xn + (ti * TILE + r) * ld + tj * TILE + 8 * ch, u32x4{lo.x, lo.y, hi.x, hi.y});
+    const u32x4 v{lo.x, lo.y, hi.x, hi.y};
+    // at TILE 128 the new iterate is written non-temporally: the tiles in
+    // flight then keep more of the cache for their operands (5 % on that
+    // launch); at 256 it measured slower
+    if constexpr (TILE == kTileSmall)
+      __builtin_nontemporal_store(v, (__attribute__((address_space(1))) u32x4*)(xn + (ti * TILE + r) * ld + tj * TILE + 8 * ch));
+    else
+      gst<u32x4>(xn + (ti * TILE + r) * ld + tj * TILE + 8 * ch, v);
   }
 }
 
