@@ -310,3 +310,37 @@ def test_plan_arguments_are_validated_on_the_host(lib):
     assert out.value is None                         # nothing was created
     assert lib.muon_plan_step(None, ctypes.c_void_p(1 << 40), None) == muon.MUON_EINVAL
     lib.muon_plan_destroy(None)                      # a no-op
+
+
+def test_workspace_buffers_are_disjoint_and_inside(lib):
+    """For seeded random lists mixing every kernel class (fused 32..128, tile
+    128, tile 256; wide, tall, square, ragged), every matrix's buffers --
+    two iterates, A, C and (short side <= 128) C_lo -- lie inside the
+    workspace, after the table, 256-byte aligned, and overlap nothing else:
+    the kernels of different matrices (and the fused class, which runs on its
+    own stream beside the tiled classes) never write the same bytes."""
+    import random
+    rng = random.Random(1234)
+    sides = [1, 7, 31, 33, 64, 100, 128, 129, 200, 256, 511, 768, 1024, 1100, 1536, 2304]
+    for trial in range(12):
+        shapes = [(rng.choice(sides), rng.choice(sides)) for _ in range(rng.randint(1, 24))]
+        total = muon.workspace_bytes(shapes)
+        spans = []
+        first = None
+        for i, (r, c) in enumerate(shapes):
+            v = muon.workspace_view(shapes, i, 5)
+            xb = v["rows_pad"] * v["cols_pad"] * 2
+            ab = v["m_pad"] ** 2 * 2
+            assert v["rows_pad"] >= r and v["cols_pad"] >= c
+            assert v["m_pad"] == min(v["rows_pad"], v["cols_pad"]) or v["tile"] != 32
+            bufs = [(v["x_off"][0], xb), (v["x_off"][1], xb), (v["a_off"], ab), (v["c_off"], ab)]
+            if v["c_lo_off"]:
+                bufs.append((v["c_lo_off"], ab))
+            for off, size in bufs:
+                assert off % 256 == 0 and 0 < off and off + size <= total, (trial, i, off, size)
+                spans.append((off, off + size, i))
+            first = min(first, min(o for o, _ in bufs)) if first is not None else min(o for o, _ in bufs)
+            assert v["nrm2_off"] + 8 <= first
+        spans.sort()
+        for (a0, a1, ia), (b0, b1, ib) in zip(spans, spans[1:]):
+            assert a1 <= b0, f"trial {trial}: buffers of matrices {ia} and {ib} overlap"
