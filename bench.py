@@ -160,8 +160,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU Muon step "
-              "(the multi-GPU sharding is a design note, not implemented); use --gpus 1",
+        print("bench.py runs on one GPU only: it measures the Muon step on a single GPU "
+              "(sharding across GPUs is described, not implemented); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
