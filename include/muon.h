@@ -202,8 +202,9 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats,
  * memset), so replays do not depend on the previous step's workspace.  Phase
  * timing (muon_timing_enable) is skipped while the stream is capturing.  A
  * plan over both fused and tiled matrices owns a stream and two events
- * (created here, released by muon_plan_destroy); a captured step forks onto
- * that stream and joins back, so the graph holds two parallel branches. */
+ * (created here, released by muon_plan_destroy, which first waits for the
+ * work its steps queued there); a captured step forks onto that stream and
+ * joins back, so the graph holds two parallel branches. */
 typedef struct muon_plan muon_plan_t;
 int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
                      const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,

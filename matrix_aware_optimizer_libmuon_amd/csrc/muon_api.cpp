@@ -252,6 +252,8 @@ int make_side(SidePair& sp) {
 }
 
 void free_side(SidePair& sp) {
+  // work a step queued on the stream runs to completion before its events go
+  if (sp.stream) (void)hipStreamSynchronize(sp.stream);
   if (sp.join) (void)hipEventDestroy(sp.join);
   if (sp.fork) (void)hipEventDestroy(sp.fork);
   if (sp.stream) (void)hipStreamDestroy(sp.stream);
