@@ -1,0 +1,196 @@
+"""CPU model of the GEMM engine's operand staging (csrc/muon_gemm.h): the
+direct global -> LDS loads of DmaFeed, the fragment reads of frag(), and the
+tile walks decode_sym / decode_full, restated here from the kernel source.
+
+For both tile sizes and both operand layouts it checks that
+  * every load stays inside the operand buffer and inside its LDS stage,
+  * the loads of one K step place each element of the TILE x 32 operand
+    slice exactly once, and every fragment read finds the element the MFMA
+    expects (row / column mn, depth k) under the stored swizzle,
+  * the tile walks visit every tile of a matrix exactly once, in range.
+A change to the engine's indexing that breaks one of these fails here, on the
+CPU, before any GPU run.  (Index arithmetic only: no kernel runs.)"""
+import numpy as np
+import pytest
+
+BK = 32
+
+
+def lanes():
+    return np.arange(64)
+
+
+# ---------------------------------------------------------------- loads ----
+def dma_elements(tile, mn_layout, ld, mn0, kt, waves=4):
+    """(mn, k) element and LDS element offset of every 16-byte piece one K
+    step loads, for an operand with leading dimension `ld` (elements)."""
+    lpw = tile // 64
+    l = lanes()
+    out_mn, out_k, out_lds = [], [], []
+    for w in range(waves):
+        for q in range(lpw):
+            lds0 = (w * lpw + q) * 512 + 8 * l          # element offset in the stage
+            if not mn_layout:
+                row = l >> 2
+                c = (l & 3) ^ (2 * ((row >> 3) & 1))
+                # byte offset: (mn0 + 16 lpw w + 16 q + row) * 2 ld + 2 BK kt + 16 c
+                mn = mn0 + 16 * lpw * w + 16 * q + row
+                k = BK * kt + 8 * c
+            else:
+                cpr, r_ = tile // 8, 512 // tile
+                row = l // cpr
+                c = (l % cpr) ^ (2 * ((r_ * (q & 1) + row) & 3) + 8 * (w & 1))
+                k = BK * kt + r_ * lpw * w + r_ * q + row
+                mn = mn0 + 8 * c
+            out_mn.append(mn)
+            out_k.append(k)
+            out_lds.append(lds0)
+    return np.concatenate(out_mn), np.concatenate(out_k), np.concatenate(out_lds)
+
+
+def stored_position(tile, mn_layout, mn_rel, k_rel):
+    """Element offset in the stage where the reader expects (mn_rel, k_rel)."""
+    if not mn_layout:
+        c = k_rel // 8
+        return mn_rel * BK + ((c ^ (2 * ((mn_rel >> 3) & 1))) * 8) + k_rel % 8
+    c = mn_rel // 8
+    return k_rel * tile + ((c ^ (2 * (k_rel & 3) + 8 * ((k_rel >> 3) & 1))) * 8) + mn_rel % 8
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("mn_layout", [False, True])
+def test_one_step_of_loads_fills_the_stage_exactly(tile, mn_layout):
+    ld = 4 * tile + 64 if not mn_layout else 3 * tile
+    mn0 = tile                                     # second tile row
+    kt = 5
+    mn, k, lds = dma_elements(tile, mn_layout, ld, mn0, kt)
+    # 8 elements per 16-byte piece
+    step = np.arange(8)
+    zero = np.zeros(8, dtype=np.int64)
+    mn_all = (mn[:, None] + (step if mn_layout else zero)).ravel()
+    k_all = (k[:, None] + (zero if mn_layout else step)).ravel()
+    lds_all = (lds[:, None] + np.arange(8)).ravel()
+    te = tile * BK
+    assert lds_all.min() >= 0 and lds_all.max() < te
+    assert len(np.unique(lds_all)) == te             # every stage element written once
+    # each LDS element receives the element the readers expect there
+    want = stored_position(tile, mn_layout, mn_all - mn0, k_all - BK * kt)
+    assert np.array_equal(want, lds_all)
+    assert mn_all.min() == mn0 and mn_all.max() == mn0 + tile - 1
+    assert k_all.min() == BK * kt and k_all.max() == BK * kt + BK - 1
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("mn_layout", [False, True])
+@pytest.mark.parametrize("extent", [(1, 1), (3, 2), (16, 9)])
+def test_loads_stay_inside_the_operand(tile, mn_layout, extent):
+    """The last tile of a matrix, every K step including the three clamped
+    steps past the end (which re-read the last step)."""
+    tiles_mn, k_steps4 = extent
+    K = 4 * BK * k_steps4                          # K is a multiple of 128
+    n_mn = tiles_mn * tile
+    ld = K if not mn_layout else n_mn
+    rows = n_mn if not mn_layout else K
+    kt_n = K // BK
+    for kt in range(kt_n + 3):
+        kc = min(kt, kt_n - 1)
+        mn, k, _ = dma_elements(tile, mn_layout, ld, n_mn - tile, kc)
+        if not mn_layout:
+            first = mn * ld + k
+            last = first + 7
+        else:
+            first = k * ld + mn
+            last = first + 7
+        assert first.min() >= 0 and last.max() < rows * ld
+
+
+# ------------------------------------------------------------ fragments ----
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("mn_layout", [False, True])
+def test_fragment_reads_find_their_elements(tile, mn_layout):
+    """frag(): lane l holds row (or column) rowbase + (l & 15), depth
+    8 (l >> 4) .. +7; K-contiguous stages are read with one 16-byte read,
+    MN-contiguous ones with two transposing 8-byte reads."""
+    l = lanes()
+    te = tile * BK
+    for rowbase in range(0, tile, 16):
+        mn_rel = rowbase + (l & 15)
+        if not mn_layout:
+            row = mn_rel
+            c = (l >> 4) ^ (2 * ((row >> 3) & 1))
+            addr = row * BK + c * 8                      # 8 elements from here
+            for j in range(8):
+                assert np.array_equal(addr + j, stored_position(tile, False, mn_rel, 8 * (l >> 4) + j))
+        else:
+            g, i = l >> 4, l & 15
+            m = rowbase + 4 * (i & 3)
+            k = 8 * g + (i >> 2)
+            off = (((m >> 3) ^ (2 * (i >> 2) + 8 * (g & 1))) << 3) + (m & 4)
+            for half, kk in enumerate((k, k + 4)):
+                base = kk * tile + off                   # 4 elements (8 bytes) per lane
+                assert base.min() >= 0 and base.max() + 3 < te
+                # the transposing read: in each 16-lane group, lane 4a + b gets
+                # element b of the pieces addressed by lanes a, a + 4, a + 8, a + 12
+                for grp in range(4):
+                    lg = np.arange(16) + 16 * grp
+                    for a in range(4):
+                        for b in range(4):
+                            dst = 16 * grp + 4 * a + b
+                            src_lanes = lg[[a, a + 4, a + 8, a + 12]]
+                            got = base[src_lanes] + b            # elements lane dst receives
+                            want = stored_position(tile, True, np.full(4, rowbase + dst % 16),
+                                                   8 * grp + 4 * half + np.arange(4))
+                            assert np.array_equal(got, want), (tile, rowbase, dst)
+
+
+# ----------------------------------------------------------- tile walks ----
+def decode_sym(u, t, gm=8):
+    lo = 0
+    while True:
+        hi = min(lo + gm, t)
+        band = (hi - lo) * t - (lo + hi - 1) * (hi - lo) // 2
+        if u < band or hi == t:
+            break
+        u -= band
+        lo = hi
+    hi = min(lo + gm, t)
+    tj = lo
+    while True:
+        rows = min(tj, hi - 1) - lo + 1
+        if u < rows or tj == t - 1:
+            break
+        u -= rows
+        tj += 1
+    return lo + u, tj
+
+
+def decode_full(u, tm, tn, gm=8):
+    group = u // (gm * tn)
+    first = group * gm
+    g = min(tm - first, gm)
+    local = u - group * gm * tn
+    return first + local % g, local // g
+
+
+@pytest.mark.parametrize("t", [1, 2, 7, 8, 9, 16, 17, 33])
+def test_symmetric_walk_covers_the_upper_triangle(t):
+    n = t * (t + 1) // 2
+    got = [decode_sym(u, t) for u in range(n)]
+    assert sorted(got) == sorted((i, j) for i in range(t) for j in range(i, t))
+
+
+@pytest.mark.parametrize("tm,tn", [(1, 1), (1, 5), (5, 1), (8, 16), (9, 3), (56, 16), (16, 56), (17, 17)])
+def test_full_walk_covers_the_grid(tm, tn):
+    got = [decode_full(u, tm, tn) for u in range(tm * tn)]
+    assert sorted(got) == [(i, j) for i in range(tm) for j in range(tn)]
+
+
+def xcd_remap(b, nb):
+    per, rem = nb >> 3, nb & 7
+    x, i = b & 7, b >> 3
+    return x * per + min(x, rem) + i
+
+
+@pytest.mark.parametrize("nb", [1, 7, 8, 9, 255, 256, 1000, 30464])
+def test_xcd_remap_is_a_permutation(nb):
+    assert sorted(xcd_remap(b, nb) for b in range(nb)) == list(range(nb))
