@@ -194,3 +194,112 @@ def xcd_remap(b, nb):
 @pytest.mark.parametrize("nb", [1, 7, 8, 9, 255, 256, 1000, 30464])
 def test_xcd_remap_is_a_permutation(nb):
     assert sorted(xcd_remap(b, nb) for b in range(nb)) == list(range(nb))
+
+
+# ------------------------------------------------------------ epilogues ----
+def tswz(col):
+    return ((col & 3) << 2) | ((col >> 2) & 3)
+
+
+def tpos(tile, row, col):
+    return col * tile + ((((row >> 2) ^ tswz(col)) << 2) | (row & 3))
+
+
+def acc_layout(tile):
+    """(row, col) of accumulator element e of block (bi, bj) for every lane of
+    every wave, as the symmetric epilogue sees them: 4 consecutive rows of
+    one column per lane and block."""
+    wt, nb = tile // 2, tile // 32
+    rows, cols = [], []
+    for w in range(4):
+        row_a, row_b = wt * (w >> 1), wt * (w & 1)
+        l = lanes()
+        for bi in range(nb):
+            for bj in range(nb):
+                rr = row_a + 16 * bi + 4 * (l >> 4)
+                cc = row_b + 16 * bj + (l & 15)
+                for e in range(4):
+                    rows.append(rr + e)
+                    cols.append(cc)
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_symmetric_epilogue_staging_and_both_stores(tile):
+    """store_sym stages each accumulator at tpos(row, col); store_staged then
+    writes the mirror (column col of the tile as a row) with 16-byte reads and
+    the tile itself (rows) with transposing reads.  Every element lands at the
+    right place of the output, and every read stays inside the staging tile."""
+    rows, cols = acc_layout(tile)
+    pos = tpos(tile, rows, cols)
+    assert len(np.unique(pos)) == tile * tile and pos.min() >= 0 and pos.max() < tile * tile
+    where = np.empty(tile * tile, dtype=np.int64)        # staging position -> row * tile + col
+    where[pos] = rows * tile + cols
+    # mirror: item (col, k) reads the 16 bytes at unit pair (2k) ^ (f & 14), then
+    # swaps the halves when f is odd; element j must be (row 8k + j, col)
+    cpl = tile // 8
+    for col in range(tile):
+        f = tswz(col)
+        for k in range(cpl):
+            base = col * tile + ((2 * k) ^ (f & 14)) * 4
+            got = where[base:base + 8]
+            if f & 1:
+                got = np.concatenate([got[4:], got[:4]])
+            assert np.array_equal(got, (8 * k + np.arange(8)) * tile + col), (col, k)
+    # tile rows: block (rb, cb), lane (g, i) addresses column cb + 8 g + (i >> 2)
+    # (and + 4), rows rb + 4 (i & 3) .. + 3; through the transposing read lane
+    # i of group g must receive row rb + i, columns cb + 8 g .. + 7
+    l = lanes()
+    g, i = l >> 4, l & 15
+    for rb in range(0, tile, 16):
+        for cb in range(0, tile, 32):
+            col = cb + 8 * g + (i >> 2)
+            for half, cc in enumerate((col, col + 4)):
+                base = tpos(tile, rb + 4 * (i & 3), cc)
+                assert base.min() >= 0 and base.max() + 3 < tile * tile
+                for grp in range(4):
+                    lg = np.arange(16) + 16 * grp
+                    for a in range(4):
+                        for b in range(4):
+                            dst = 4 * a + b
+                            got = where[base[lg[[a, a + 4, a + 8, a + 12]]] + b]
+                            want = (rb + dst) * tile + cb + 8 * grp + 4 * half + np.arange(4)
+                            assert np.array_equal(got, want), (rb, cb, grp, dst)
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_x_update_epilogue_staging(tile):
+    """k_xupdate stages lane (row rl + 16 bi, columns cl + 16 bj .. + 3) as one
+    8-byte unit u = col / 4 at unit u ^ (row & 31) of its row, then writes
+    16-byte row chunks; each chunk must hold columns 8 ch .. 8 ch + 7."""
+    wt, nb = tile // 2, tile // 32
+    units = tile // 4
+    where = -np.ones((tile, units), dtype=np.int64)
+    for w in range(4):
+        l = lanes()
+        rl = wt * (w >> 1) + (l & 15)
+        cl = wt * (w & 1) + 4 * (l >> 4)
+        for bi in range(nb):
+            for bj in range(nb):
+                r = rl + 16 * bi
+                u = (cl + 16 * bj) >> 2
+                phys = u ^ (r & 31)
+                assert phys.max() < units
+                assert (where[r, phys] == -1).all()
+                where[r, phys] = u
+    assert (where >= 0).all()
+    for r in range(tile):
+        for ch in range(tile // 8):
+            assert where[r, (2 * ch) ^ (r & 31)] == 2 * ch
+            assert where[r, (2 * ch + 1) ^ (r & 31)] == 2 * ch + 1
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_c_epilogue_reads_its_tile_of_a(tile):
+    """k_gram2 reads A[c0 + cc][r0 + rr .. + 3] (the tile's own A values, by
+    symmetry) for every accumulator: inside A for the last tile pair."""
+    rows, cols = acc_layout(tile)
+    m_pad = 3 * tile
+    r0 = c0 = m_pad - tile
+    first = (c0 + cols) * m_pad + r0 + (rows & ~3)
+    assert first.min() >= 0 and (first + 3).max() < m_pad * m_pad
