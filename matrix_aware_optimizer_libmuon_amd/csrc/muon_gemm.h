@@ -81,6 +81,17 @@ struct Opnd {
   int64_t ld;
 };
 
+// The work-item index as a value the compiler cannot re-derive: the lane-
+// dependent LDS and global offsets are then formed once per tile and kept in
+// registers, instead of being recomputed from the index inside the K loop
+// (6-7 vector ALU instructions per 64 MFMAs instead of 33-35 where both
+// operands are K-contiguous; 1-3 % on the Gram, C and X-update launches).
+__device__ __forceinline__ int opaque_tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Global -> LDS, 16 bytes per lane, without registers: lane l's 16 bytes at
 // sbase + voff land at LDS byte 16 l of the 1 KB block at lds_dst.  Written
 // as a one-line asm statement: it writes only LDS (no register results),
@@ -120,9 +131,10 @@ struct DmaFeed {
   const char* base;
   int64_t qstride, kstep;
   uint32_t voff[2];
-  __device__ __forceinline__ DmaFeed(const Opnd& op, int64_t mn0) {
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int w;
+  __device__ __forceinline__ DmaFeed(const Opnd& op, int64_t mn0, int tid) {
+    const int lane = tid & 63;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t ldb = op.ld * 2;
     const char* p = reinterpret_cast<const char*>(op.p);
     if constexpr (!MN) {
@@ -146,7 +158,6 @@ struct DmaFeed {
   }
   // block q of step kt into the operand tile at `tile`
   __device__ __forceinline__ void load(int64_t kt, int q, uint16_t* tile) const {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     dma16(base + kt * kstep + q * qstride, voff[q & 1], tile + (w * LPW + q) * 512);
   }
 };
@@ -154,8 +165,7 @@ struct DmaFeed {
 // MFMA operand fragment: 16 rows from rowbase, k = 0 .. 31 of a staged tile;
 // lane l holds row rowbase + (l & 15), k = 8 (l >> 4) .. +7.
 template <bool MN, int TILE>
-__device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ bf16x8_t frag(const uint16_t* tile, int rowbase, int lane) {
   if constexpr (!MN) {
     const int row = rowbase + (lane & 15);
     const int c = (lane >> 4) ^ (2 * ((row >> 3) & 1));
@@ -220,7 +230,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int TILE, bool PMN, bool QMN, bool SWAP = false>
 __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t mp0, int64_t nq0,
                                           int64_t K, uint16_t* smem,
-                                          f32x4_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB]) {
+                                          f32x4_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB], int tid) {
   using G = Geo<TILE>;
   constexpr int NB = G::NB, H = NB / 2, PASS = H * NB, SLOTS = NB * NB;
   constexpr int LPS = 2 * G::LPW;                                // loads per wave per step
@@ -230,10 +240,10 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
   // spreading measured no better)
   constexpr int LSS = TILE == 256 ? (SLOTS - H) / LPS : ((PASS - H) / LPS > 0 ? (PASS - H) / LPS : 1);
   static_assert(H + (LPS - 1) * LSS < SLOTS, "load slots exceed the step");
-  const int w = threadIdx.x >> 6;
+  const int w = tid >> 6, lane = tid & 63;
   const int rowA = G::WT * (w >> 1), rowB = G::WT * (w & 1);
-  const DmaFeed<PMN, TILE> fp(P, mp0);
-  const DmaFeed<QMN, TILE> fq(Q, nq0);
+  const DmaFeed<PMN, TILE> fp(P, mp0, tid);
+  const DmaFeed<QMN, TILE> fq(Q, nq0, tid);
   bf16x8_t fa[NB], fb[NB];
   const int64_t kt_n = K / BK;
   auto stage = [&](int64_t kt) { return smem + static_cast<int>(kt & (kStages - 1)) * (2 * G::TE); };
@@ -251,9 +261,9 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
   vm_wait<(kStages - 2) * LPS>();
   lds_barrier();
 #pragma unroll
-  for (int r = 0; r < H; ++r) fa[r] = frag<PMN, TILE>(smem, rowA + 16 * r);
+  for (int r = 0; r < H; ++r) fa[r] = frag<PMN, TILE>(smem, rowA + 16 * r, lane);
 #pragma unroll
-  for (int r = 0; r < NB; ++r) fb[r] = frag<QMN, TILE>(smem + G::TE, rowB + 16 * r);
+  for (int r = 0; r < NB; ++r) fb[r] = frag<QMN, TILE>(smem + G::TE, rowB + 16 * r, lane);
 
   for (int64_t kt = 0; kt < kt_n; ++kt) {
     vm_wait<LPS>();   // step kt+1 has landed (kt+2 may be in flight)
@@ -265,9 +275,9 @@ __device__ __forceinline__ void gemm_tile(const Opnd& P, const Opnd& Q, int64_t 
       constexpr int bi = pass * H + sp % H, bj = sp / H;
       acc[bi][bj] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[bj], fa[bi], acc[bi][bj], 0, 0, 0)
                          : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
-      if constexpr (s < H) fa[H + s] = frag<PMN, TILE>(cu, rowA + 16 * (H + s));
-      if constexpr (s >= PASS && s < PASS + H) fa[s - PASS] = frag<PMN, TILE>(nx, rowA + 16 * (s - PASS));
-      if constexpr (pass == 1 && sp % H == H - 1) fb[bj] = frag<QMN, TILE>(nx + G::TE, rowB + 16 * bj);
+      if constexpr (s < H) fa[H + s] = frag<PMN, TILE>(cu, rowA + 16 * (H + s), lane);
+      if constexpr (s >= PASS && s < PASS + H) fa[s - PASS] = frag<PMN, TILE>(nx, rowA + 16 * (s - PASS), lane);
+      if constexpr (pass == 1 && sp % H == H - 1) fb[bj] = frag<QMN, TILE>(nx + G::TE, rowB + 16 * bj, lane);
       if constexpr (s >= H && (s - H) % LSS == 0 && (s - H) / LSS < LPS)
         load(kt + kStages - 1, (s - H) / LSS);
       __builtin_amdgcn_sched_barrier(0);
@@ -300,8 +310,8 @@ __device__ __forceinline__ int tpos(int row, int col) {
 // transpose at (c0, r0) when `mirror`.
 template <int TILE>
 __device__ __forceinline__ void store_staged(const uint16_t* T, uint16_t* out, int64_t ld,
-                                             int64_t r0, int64_t c0, bool mirror) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+                                             int64_t r0, int64_t c0, bool mirror, int tid) {
+  const int t = tid, lane = t & 63, w = t >> 6;
   if (mirror) {  // out[c0 + col][r0 + 8k .. +7] = T[col][8k .. 8k+7]
     constexpr int CPL = TILE / 8;
 #pragma unroll 4
@@ -340,10 +350,10 @@ __device__ __forceinline__ void store_staged(const uint16_t* T, uint16_t* out, i
 // and written as the columns of the lower block (a, b), a > b; a diagonal
 // block keeps its upper half and mirrors it into its lower half.
 template <int TILE>
-__device__ __forceinline__ void symmetrize(uint16_t* T) {
+__device__ __forceinline__ void symmetrize(uint16_t* T, int tid) {
   constexpr int U = TILE / 4;                 // 4 x 4 blocks per side
   constexpr int NBLK = U * (U + 1) / 2;       // blocks on or below the diagonal
-  for (int idx = threadIdx.x; idx < NBLK; idx += kGemmThreads) {
+  for (int idx = tid; idx < NBLK; idx += kGemmThreads) {
     int a = static_cast<int>((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
     if (a * (a + 1) / 2 > idx) --a;
     if ((a + 1) * (a + 2) / 2 <= idx) ++a;
@@ -375,11 +385,11 @@ template <int TILE, bool GRAM2>
 __device__ __forceinline__ void store_sym(const f32x4_t (&acc)[Geo<TILE>::NB][Geo<TILE>::NB],
                                           uint16_t* smem, uint16_t* out, uint16_t* out_lo,
                                           const uint16_t* src, int64_t ld, int64_t ti, int64_t tj,
-                                          float a, float b, float c) {
+                                          float a, float b, float c, int tid) {
   constexpr int NB = Geo<TILE>::NB;
   const bool diag = ti == tj;
   const int64_t r0 = ti * TILE, c0 = tj * TILE;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int rowA = Geo<TILE>::WT * (w >> 1), rowB = Geo<TILE>::WT * (w & 1);
   // GRAM2: every A value the tile needs, loaded up front (one memory round
   // trip instead of one per block).  A is symmetric, so A[r0+rr+e][c0+cc] =
@@ -431,10 +441,10 @@ __device__ __forceinline__ void store_sym(const f32x4_t (&acc)[Geo<TILE>::NB][Ge
         }
     lds_barrier();
     if (diag) {
-      symmetrize<TILE>(smem);
+      symmetrize<TILE>(smem, tid);
       lds_barrier();
     }
-    store_staged<TILE>(smem, pass == 0 ? out : out_lo, ld, r0, c0, !diag);
+    store_staged<TILE>(smem, pass == 0 ? out : out_lo, ld, r0, c0, !diag, tid);
     lds_barrier();
   }
 }
@@ -483,19 +493,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gram(const MatDesc* __restrict
                                                        int64_t units, int parity) {
   using G = Geo<TILE>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * G::TE];
+  const int tid = opaque_tid();
   const int64_t unit = xcd_remap(blockIdx.x, units);
-  const int i = find_matrix(prefix, n, unit);
-  const MatDesc& d = descs[i];
+  const int mi = find_matrix(prefix, n, unit);
+  const MatDesc& d = descs[mi];
   int64_t ti, tj;
-  decode_sym(unit - prefix[i], d.m_pad / TILE, ti, tj);
+  decode_sym(unit - prefix[mi], d.m_pad / TILE, ti, tj);
   const Opnd X{d.x[parity], d.cols_pad};
   f32x4_t acc[G::NB][G::NB];
   zero_acc<G::NB>(acc);
   if (d.flags & kFlagTall)
-    gemm_tile<TILE, true, true>(X, X, ti * TILE, tj * TILE, d.rows_pad, smem, acc);
+    gemm_tile<TILE, true, true>(X, X, ti * TILE, tj * TILE, d.rows_pad, smem, acc, tid);
   else
-    gemm_tile<TILE, false, false>(X, X, ti * TILE, tj * TILE, d.cols_pad, smem, acc);
-  store_sym<TILE, false>(acc, smem, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f);
+    gemm_tile<TILE, false, false>(X, X, ti * TILE, tj * TILE, d.cols_pad, smem, acc, tid);
+  store_sym<TILE, false>(acc, smem, d.a, nullptr, nullptr, d.m_pad, ti, tj, 0.f, 0.f, 0.f, tid);
 }
 
 // K3b: C = a I + b A + c A A  (A symmetric: A A = A A^T, a K-contiguous product).
@@ -507,18 +518,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gram2(const MatDesc* __restric
                                                         int64_t units, float a, float b, float c) {
   using G = Geo<TILE>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * G::TE];
+  const int tid = opaque_tid();
   const int64_t unit = xcd_remap(blockIdx.x, units);
-  const int i = find_matrix(prefix, n, unit);
-  const MatDesc& d = descs[i];
+  const int mi = find_matrix(prefix, n, unit);
+  const MatDesc& d = descs[mi];
   int64_t ti, tj;
-  decode_sym(unit - prefix[i], d.m_pad / TILE, ti, tj);
+  decode_sym(unit - prefix[mi], d.m_pad / TILE, ti, tj);
   const Opnd A{d.a, d.m_pad};
   f32x4_t acc[G::NB][G::NB];
   zero_acc<G::NB>(acc);
-  gemm_tile<TILE, false, false>(A, A, ti * TILE, tj * TILE, d.m_pad, smem, acc);
+  gemm_tile<TILE, false, false>(A, A, ti * TILE, tj * TILE, d.m_pad, smem, acc, tid);
   // the hi/lo split only exists for short sides <= 128, i.e. in the 128 class
   uint16_t* lo = (TILE == kTileSmall && (d.flags & kFlagSplitC)) ? d.blo : nullptr;
-  store_sym<TILE, true>(acc, smem, d.b, lo, d.a, d.m_pad, ti, tj, a, b, c);
+  store_sym<TILE, true>(acc, smem, d.b, lo, d.a, d.m_pad, ti, tj, a, b, c, tid);
 }
 
 // K4: X' = C X.  Wide (rows <= cols): X'[i][k] = sum_j C[i][j] X[j][k].
@@ -530,11 +542,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
                                                           int n, int64_t units, int parity) {
   using G = Geo<TILE>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * G::TE];
+  const int tid = opaque_tid();
   const int64_t unit = xcd_remap(blockIdx.x, units);
-  const int i = find_matrix(prefix, n, unit);
-  const MatDesc& d = descs[i];
+  const int mi = find_matrix(prefix, n, unit);
+  const MatDesc& d = descs[mi];
   int64_t ti, tj;
-  decode_full(unit - prefix[i], d.rows_pad / TILE, d.cols_pad / TILE, ti, tj);
+  decode_full(unit - prefix[mi], d.rows_pad / TILE, d.cols_pad / TILE, ti, tj);
   const uint16_t* x = d.x[parity];
   uint16_t* xn = d.x[parity ^ 1];
   const int64_t ld = d.cols_pad;
@@ -544,10 +557,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
   zero_acc<G::NB>(acc);
   if (d.flags & kFlagTall) {
     gemm_tile<TILE, false, false, true>(Opnd{x, ld}, Opnd{d.b, d.m_pad}, ti * TILE, tj * TILE,
-                                        d.m_pad, smem, acc);
+                                        d.m_pad, smem, acc, tid);
     if (split)
       gemm_tile<TILE, false, false, true>(Opnd{x, ld}, Opnd{d.blo, d.m_pad}, ti * TILE, tj * TILE,
-                                          d.m_pad, smem, acc);
+                                          d.m_pad, smem, acc, tid);
   } else {
     // C is exactly symmetric, so its rows may also be read as MN-contiguous
     // columns.  At TILE = 128 both operands take the transpose-read path
@@ -555,17 +568,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
     // its cheaper 16-byte fragment reads.
     constexpr bool kCmn = TILE == kTileSmall;
     gemm_tile<TILE, kCmn, true, true>(Opnd{d.b, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
-                                      d.m_pad, smem, acc);
+                                      d.m_pad, smem, acc, tid);
     if (split)
       gemm_tile<TILE, kCmn, true, true>(Opnd{d.blo, d.m_pad}, Opnd{x, ld}, ti * TILE, tj * TILE,
-                                        d.m_pad, smem, acc);
+                                        d.m_pad, smem, acc, tid);
   }
   // Stage the bf16 tile in LDS, row-major with 8-byte units XORed by the row
   // (unit u of row r at u ^ (r & 31): a staging write, 32 rows at one unit,
   // then covers all banks), and write it out as whole 16-byte row chunks.
   // Transposed blocks: lane holds row rowA + 16 bi + (lane & 15), columns
   // rowB + 16 bj + 4 (lane >> 4) .. +3.
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int rl = G::WT * (w >> 1) + (lane & 15);
   const int cl = G::WT * (w & 1) + 4 * (lane >> 4);
 #pragma unroll
@@ -581,7 +594,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_xupdate(const MatDesc* __restr
   lds_barrier();
   constexpr int CPR = TILE / 8;  // 16-byte chunks per row
 #pragma unroll 4
-  for (int idx = threadIdx.x; idx < TILE * CPR; idx += kGemmThreads) {
+  for (int idx = tid; idx < TILE * CPR; idx += kGemmThreads) {
     const int r = idx / CPR, ch = idx % CPR;
     const u32x2 lo = *reinterpret_cast<const u32x2*>(smem + r * TILE + (((2 * ch) ^ (r & 31)) << 2));
     const u32x2 hi = *reinterpret_cast<const u32x2*>(smem + r * TILE + (((2 * ch + 1) ^ (r & 31)) << 2));
