@@ -47,6 +47,11 @@
  * after MUON_EHIP it includes the HIP error text of the calling thread's last
  * failure.
  *
+ * Device: a call works on the calling thread's current HIP device.  Its
+ * stream must belong to that device (else MUON_EINVAL, before anything is
+ * launched), and so must every buffer it is given (not checkable here: a
+ * pointer into another device's memory is the caller's error).
+ *
  * Thread safety: calls may come from several host threads; two calls that
  * run concurrently must use different workspaces.
  *

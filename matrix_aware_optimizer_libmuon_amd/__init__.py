@@ -107,6 +107,12 @@ def workspace_view(shapes: Sequence, index: int, ns_steps: int) -> dict:
             "tile": v.tile}
 
 
+def _on(device):
+    """The tensors' device as the current one for the duration of a library
+    call (the library works on the calling thread's current device)."""
+    return _torch().cuda.device(device)
+
+
 def _stream_handle(stream, device):
     torch = _torch()
     if stream is None:
@@ -141,13 +147,14 @@ def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 
     lib = _lib.load()
     ws_args = (ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
                _stream_handle(stream, device))
-    if flags:
-        opts = MuonOptions(flags, 0)
-        st = lib.muon_step_ex(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
-                              mode, float(eps), ctypes.byref(opts), *ws_args)
-    else:
-        st = lib.muon_step(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
-                           mode, float(eps), *ws_args)
+    with _on(device):
+        if flags:
+            opts = MuonOptions(flags, 0)
+            st = lib.muon_step_ex(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
+                                  mode, float(eps), ctypes.byref(opts), *ws_args)
+        else:
+            st = lib.muon_step(arr, n, float(lr), float(mu), float(wd), int(ns_steps), carr, nc,
+                               mode, float(eps), *ws_args)
     _lib.check(st, "muon_step")
     return workspace
 
@@ -186,10 +193,11 @@ class Plan:
         carr, nc = _coeff_array(coeffs, ns_steps)
         self._lib = _lib.load()
         handle = ctypes.c_void_p()
-        st = self._lib.muon_plan_create(arr, n, int(ns_steps), carr, nc, mode, float(eps),
-                                        ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream_handle(stream, self.device), ctypes.byref(handle))
+        with _on(self.device):
+            st = self._lib.muon_plan_create(arr, n, int(ns_steps), carr, nc, mode, float(eps),
+                                            ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream, self.device), ctypes.byref(handle))
         _lib.check(st, "muon_plan_create")
         self._handle = handle
 
@@ -203,9 +211,10 @@ class Plan:
     def step(self, stream=None) -> None:
         if not self._handle:
             raise RuntimeError("plan is closed")
-        _lib.check(self._lib.muon_plan_step(self._handle, ctypes.c_void_p(self.hyper.data_ptr()),
-                                            _stream_handle(stream, self.device)),
-                   "muon_plan_step")
+        with _on(self.device):
+            st = self._lib.muon_plan_step(self._handle, ctypes.c_void_p(self.hyper.data_ptr()),
+                                          _stream_handle(stream, self.device))
+        _lib.check(st, "muon_plan_step")
 
     def close(self) -> None:
         if getattr(self, "_handle", None):
@@ -230,10 +239,11 @@ def orthogonalize(inputs: Sequence, outputs: Sequence | None = None, *, ns_steps
     if workspace is None:
         workspace = alloc_workspace([tuple(t.shape) for t in inputs], device)
     carr, nc = _coeff_array(coeffs, ns_steps)
-    st = _lib.load().muon_orthogonalize(arr, n, int(ns_steps), carr, nc, float(eps),
-                                        ctypes.c_void_p(workspace.data_ptr()),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream_handle(stream, device))
+    with _on(device):
+        st = _lib.load().muon_orthogonalize(arr, n, int(ns_steps), carr, nc, float(eps),
+                                            ctypes.c_void_p(workspace.data_ptr()),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream, device))
     _lib.check(st, "muon_orthogonalize")
     return outputs
 
@@ -270,10 +280,11 @@ def adamw_step(params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg_sq
     device = params[0].device if n else torch.device("cuda")
     if workspace is None:
         workspace = alloc_adamw_workspace(n, device)
-    st = _lib.load().muon_adamw_step(arr, n, float(lr), float(betas[0]), float(betas[1]), float(eps),
-                                     float(wd), ctypes.c_void_p(workspace.data_ptr()),
-                                     workspace.numel() * workspace.element_size(),
-                                     _stream_handle(stream, device))
+    with _on(device):
+        st = _lib.load().muon_adamw_step(arr, n, float(lr), float(betas[0]), float(betas[1]),
+                                         float(eps), float(wd), ctypes.c_void_p(workspace.data_ptr()),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream, device))
     _lib.check(st, "muon_adamw_step")
     return workspace
 

@@ -183,6 +183,15 @@ int hip_fail(hipError_t e, const char* what) {
   return MUON_EHIP;
 }
 
+// False when `stream` belongs to another device than `dev` (a launch there
+// would run the library's work on the wrong device).  A stream the runtime
+// cannot place (the null stream) is taken as the current device's.
+bool stream_on_device(hipStream_t stream, int dev) {
+  hipDevice_t sdev = 0;
+  if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return true;
+  return static_cast<int>(sdev) == dev;
+}
+
 int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -193,6 +202,7 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   e = hipStreamIsCapturing(stream, &cap);
   if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
   if (cap != hipStreamCaptureStatusNone) return MUON_ECAPTURE;
+  if (!stream_on_device(stream, dev)) return MUON_EINVAL;
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   Slot& s = st.slots[st.next];
@@ -725,7 +735,7 @@ int muon_plan_step(const muon_plan_t* plan, const float* hyper, hipStream_t stre
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev != plan->device) return MUON_EINVAL;
+  if (dev != plan->device || !stream_on_device(stream, dev)) return MUON_EINVAL;
   if (plan->t.n_active == 0) return MUON_OK;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   e = hipStreamIsCapturing(stream, &cap);
