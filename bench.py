@@ -13,6 +13,8 @@ input already resident in HBM.  Prints ONE JSON line:
 * roofline: the dominant kernel's algorithmic work per launch over its
   average launch time (HIP events on the launch stream, inside the timed
   region) against its roofline;
+* measured_ceiling: second denominators measured on this GPU (the
+  platform's bf16 GEMM on the X-update products, a device copy);
 * cpu_baseline: the fp64 oracle timed on a bounded sample of the same
   workload on this host.
 """
@@ -112,6 +114,66 @@ def cpu_baseline(w, target_s: float = 20.0):
                       f"step each (numpy, BLAS threads={cores}); input generation excluded"}
 
 
+def measured_ceilings(torch, muon, w, dev, reps: int = 10):
+    """Second denominators, measured on this GPU: the platform's bf16 GEMM
+    (torch.matmul, i.e. hipBLASLt, as a black box) on the X-update products
+    of the workload's tiled matrices, weighted like the launch (the faster of
+    its NN and NT forms for the tall product, since C is symmetric), and a
+    plain device copy for HBM."""
+    shapes = {}
+    for r, c in w.shapes:
+        if muon.workspace_view([(r, c)], 0, w.ns_steps)["tile"] == FUSED_TILE:
+            continue
+        shapes[(r, c)] = shapes.get((r, c), 0) + 1
+    out = {}
+
+    def timed(f):
+        for _ in range(3):
+            f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    if shapes:
+        flops = secs = 0.0
+        per = {}
+        for (r, c), count in shapes.items():
+            m, n = min(r, c), max(r, c)
+            cm = torch.randn(m, m, device=dev).to(torch.bfloat16)
+            cm = ((cm + cm.t()) * 0.5).contiguous()
+            if r <= c:                       # X' = C X, X stored m x n
+                x = torch.randn(m, n, device=dev).to(torch.bfloat16)
+                o = torch.empty(m, n, device=dev, dtype=torch.bfloat16)
+                t = timed(lambda: torch.matmul(cm, x, out=o))
+            else:                            # X'^T = X^T C, stored n x m
+                x = torch.randn(n, m, device=dev).to(torch.bfloat16)
+                o = torch.empty(n, m, device=dev, dtype=torch.bfloat16)
+                t = min(timed(lambda: torch.matmul(x, cm, out=o)),
+                        timed(lambda: torch.matmul(x, cm.t(), out=o)))
+            del cm, x, o
+            per[f"{r}x{c}"] = 2 * m * m * n / t / 1e12
+            flops += count * 2 * m * m * n
+            secs += count * t
+        out["x_update_vendor_gemm_tflops"] = flops / secs / 1e12
+        out["vendor_gemm_tflops_by_shape"] = per
+    n = 2**29                                # 2 GiB of fp32
+    a = torch.ones(n, device=dev)
+    b = torch.empty_like(a)
+    t = timed(lambda: b.copy_(a))
+    out["hbm_copy_gbs"] = 2 * 4 * n / t / 1e9
+    del a, b
+    out["method"] = ("torch.matmul (hipBLASLt) bf16 on the same products, one call per "
+                     f"matrix, 3 warm-up + {reps} timed calls each (launch-bound for small "
+                     "matrices, so there the fraction measures grouping as much as the "
+                     "kernel); device copy of 2 GiB (read + write)")
+    return out
+
+
 def bench_adamw(torch, muon, dev, reps: int = 10):
     """AdamW branch on the parameters Muon does not take, for the d=4096
     transformer: token embedding and output head (32000 x 4096 each; the
@@ -155,6 +217,8 @@ def main():
     ap.add_argument("--no-phase-timing", action="store_true")
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip the AdamW-branch measurement (an extra object in the JSON line)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured second denominators (vendor GEMM, device copy)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -278,6 +342,14 @@ def main():
 
     del params, grads, moms, ws
     torch.cuda.empty_cache()
+    if not args.no_ceilings:
+        ceil = measured_ceilings(torch, muon, w, dev)
+        if "roofline" in out and out["roofline"]["kernel"] == "x_update" and \
+                "x_update_vendor_gemm_tflops" in ceil:
+            ceil["x_update_frac_of_vendor"] = (out["roofline"]["achieved"]
+                                               / ceil["x_update_vendor_gemm_tflops"])
+        out["measured_ceiling"] = ceil
+        torch.cuda.empty_cache()
     if not args.no_adamw:
         out["adamw"] = bench_adamw(torch, muon, dev)
     torch.cuda.empty_cache()
