@@ -391,23 +391,44 @@ __device__ __forceinline__ void store_sym(const f32x4_t (&acc)[Geo<TILE>::NB][Ge
   const int64_t r0 = ti * TILE, c0 = tj * TILE;
   const int lane = tid & 63, w = tid >> 6;
   const int rowA = Geo<TILE>::WT * (w >> 1), rowB = Geo<TILE>::WT * (w & 1);
-  // GRAM2: every A value the tile needs, loaded up front (one memory round
-  // trip instead of one per block).  A is symmetric, so A[r0+rr+e][c0+cc] =
-  // A[c0+cc][r0+rr+e]: rows rr .. rr+3 of column cc are one 8-byte load.
-  // (At TILE = 128 the loads stay next to their use: the extra registers
-  // would cost the second resident block per CU.)
+  // GRAM2: A is symmetric, so A[r0+rr+e][c0+cc] = A[c0+cc][r0+rr+e]: the
+  // values a lane needs for rows rr .. rr+3 of column cc are 8 contiguous
+  // bytes of the mirrored tile.  At TILE = 256 every value is fetched up
+  // front (one memory round trip): the mirrored tile comes into LDS by
+  // whole-line direct loads (a wave instruction moves two A rows of 512
+  // bytes; an 8-byte gather per block would touch 16 lines per instruction
+  // and hold up the address unit), laid out [cc][rr] with its 16-byte units
+  // XOR-rotated by cc & 15, so that the 8-byte reads of a half-wave (16
+  // columns x two row pieces) touch every bank once.  (At TILE = 128 the
+  // loads stay next to their use: the extra registers would cost the second
+  // resident block per CU.)
   constexpr bool kBatch = GRAM2 && TILE == kTileBig;
   // Block (bi, bj): lane holds rows rr .. rr+3 of column cc (tile coordinates).
   auto rrow = [&](int bi) { return rowA + 16 * bi + 4 * (lane >> 4); };
   auto rcol = [&](int bj) { return rowB + 16 * bj + (lane & 15); };
   u32x2 asrc[kBatch ? NB : 1][kBatch ? NB : 1];
   if constexpr (kBatch) {
+    constexpr int UPC = TILE / 8;             // 16-byte units per column
+    constexpr int CPB = 64 / UPC;             // columns per 1 KB wave load
+    constexpr int BPW = TILE / CPB / 4;       // wave loads per wave
+    const uint32_t lb = static_cast<uint32_t>(ld * 2);
+#pragma unroll 8
+    for (int q = 0; q < BPW; ++q) {
+      const int blk = w * BPW + q, col = blk * CPB + lane / UPC, u = lane % UPC;
+      dma16(reinterpret_cast<const char*>(src + (c0 + blk * CPB) * ld + r0),
+            (lane / UPC) * lb + 16u * static_cast<uint32_t>(u ^ (col & 15)), smem + blk * 512);
+    }
+    vm_wait<0>();
+    lds_barrier();
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < NB; ++bj)
-        asrc[bi][bj] = gld<u32x2>(src + (c0 + rcol(bj)) * ld + r0 + rrow(bi));
-    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first use
+      for (int bj = 0; bj < NB; ++bj) {
+        const int rr = rrow(bi), cc = rcol(bj);
+        asrc[bi][bj] = *reinterpret_cast<const u32x2*>(
+            smem + cc * TILE + ((((rr >> 3) ^ (cc & 15)) << 3) | (rr & 7)));
+      }
+    lds_barrier();                            // the staging below reuses the LDS
   }
   for (int pass = 0; pass < ((GRAM2 && out_lo) ? 2 : 1); ++pass) {
 #pragma unroll

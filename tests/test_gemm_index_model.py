@@ -303,3 +303,73 @@ def test_c_epilogue_reads_its_tile_of_a(tile):
     r0 = c0 = m_pad - tile
     first = (c0 + cols) * m_pad + r0 + (rows & ~3)
     assert first.min() >= 0 and (first + 3).max() < m_pad * m_pad
+
+
+def c_epilogue_a_staging(tile, ld, r0, c0):
+    """At TILE 256, store_sym<GRAM2> brings the mirrored A tile into LDS with
+    direct loads: wave w, load q covers 1 KB block blk = w BPW + q (columns
+    blk CPB .. + CPB - 1, CPB = 64 / (tile / 8)); lane l reads 16 bytes of A
+    row c0 + col at column r0 + 8 (u ^ (col & 15)), u = l % (tile / 8), and
+    they land at LDS element 512 blk + 8 l.  Returns, per 16-byte piece, the
+    A element offset of its first element and its LDS element offset."""
+    upc = tile // 8
+    cpb = 64 // upc
+    bpw = tile // cpb // 4
+    l = lanes()
+    src, dst = [], []
+    for w in range(4):
+        for q in range(bpw):
+            blk = w * bpw + q
+            col = blk * cpb + l // upc
+            u = l % upc
+            base = (c0 + blk * cpb) * ld + r0                  # wave-uniform, elements
+            voff_bytes = (l // upc) * 2 * ld + 16 * (u ^ (col & 15))
+            assert (voff_bytes < 2**32).all()
+            src.append(base + voff_bytes // 2)
+            dst.append(512 * blk + 8 * l)
+    return np.concatenate(src), np.concatenate(dst)
+
+
+def test_c_epilogue_a_tile_staging():
+    """The staged copy holds every element of the mirrored tile exactly once,
+    inside A and inside the 128 KB of LDS, and the 8-byte read of each
+    accumulator's A values (rows rr .. rr + 3 of column cc at unit
+    (rr >> 3) ^ (cc & 15)) finds A[c0 + cc][r0 + rr .. rr + 3]."""
+    tile = 256
+    m_pad = 3 * tile
+    for r0, c0 in ((0, 0), (m_pad - tile, 0), (0, m_pad - tile), (m_pad - tile, m_pad - tile)):
+        src, dst = c_epilogue_a_staging(tile, m_pad, r0, c0)
+        assert src.min() >= 0 and (src + 7).max() < m_pad * m_pad
+        assert dst.min() >= 0 and (dst + 7).max() < tile * tile
+        assert len(np.unique(dst)) == len(dst) == tile * tile // 8
+        lds = np.full(tile * tile, -1, dtype=np.int64)       # LDS element -> A offset
+        for j in range(8):
+            lds[dst + j] = src + j
+        assert (lds >= 0).all()
+        want = ((c0 + np.arange(tile))[:, None] * m_pad + r0 + np.arange(tile)[None, :]).ravel()
+        assert np.array_equal(np.sort(lds), np.sort(want))
+        rows, cols = acc_layout(tile)                          # per block: e = 0 .. 3, 64 lanes each
+        first = (np.arange(len(rows)) // 64) % 4 == 0
+        rr, cc = rows[first], cols[first]                      # first row of each piece
+        assert (rr % 4 == 0).all()
+        pos = cc * tile + ((((rr >> 3) ^ (cc & 15)) << 3) | (rr & 7))
+        for e in range(4):
+            assert np.array_equal(lds[pos + e], (c0 + cc) * m_pad + r0 + rr + e)
+
+
+def test_c_epilogue_a_reads_are_bank_conflict_free():
+    """Each 32-lane half of a wave's 8-byte read of the staged A tile touches
+    each of the 64 four-byte banks exactly once."""
+    tile, wt, nb = 256, 128, 8
+    l = lanes()
+    for w in range(4):
+        row_a, row_b = wt * (w >> 1), wt * (w & 1)
+        for bi in range(nb):
+            for bj in range(nb):
+                rr = row_a + 16 * bi + 4 * (l >> 4)
+                cc = row_b + 16 * bj + (l & 15)
+                byte = 2 * (cc * tile + ((((rr >> 3) ^ (cc & 15)) << 3) | (rr & 7)))
+                banks = np.stack([(byte // 4) % 64, (byte // 4 + 1) % 64], axis=1)
+                for half in (slice(0, 32), slice(32, 64)):
+                    b = banks[half].ravel()
+                    assert len(np.unique(b)) == 64, (w, bi, bj)
