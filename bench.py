@@ -91,17 +91,15 @@ def cpu_baseline(w, target_s: float = 20.0):
             seen.add(s)
             order.append(i)
     order.sort(key=lambda i: w.shapes[i][0] * w.shapes[i][1])
-    t0 = time.perf_counter()
     flops = 0
     done = []
     for idx in order:
-        mi = W.matrix_inputs(w, idx)
+        mi = W.matrix_inputs(w, idx)          # input generation is not timed
         r, c = w.shapes[idx]
         m, n = min(r, c), max(r, c)
         ts = time.perf_counter()
         O.muon_step_matrix(mi.param, mi.grad, mi.mom, lr=w.lr, mu=w.mu, wd=w.wd,
                            ns_steps=w.ns_steps, eps=w.eps, rms_mode=w.rms_mode)
-        t0 += 0  # generation time is excluded below
         done.append((idx, time.perf_counter() - ts))
         flops += w.ns_steps * (4 * m * m * n + 2 * m ** 3)
         if sum(t for _, t in done) > target_s:
