@@ -27,7 +27,8 @@ decay).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, invariants and textbook routines (numpy's SVD), not against
-itself.
+itself; ``tests/test_oracle_vs_torch_muon.py`` checks the whole step against
+PyTorch's own ``torch.optim.Muon`` on the CPU.
 """
 from __future__ import annotations
 
