@@ -14,6 +14,14 @@ computation runs in libmuon.so.
     opt = Muon([{"params": hidden_2d},
                 {"params": others, "muon": False}])
     loss.backward(); opt.step(); opt.zero_grad()
+
+For code written against PyTorch's own ``torch.optim.Muon`` the constructor
+also takes its keyword names: ``weight_decay`` (= ``wd``), ``ns_coefficients``
+(= ``coeffs``) and ``adjust_lr_fn="original"`` (= ``rms_scale="sqrt_max1"``,
+the update scaled by sqrt(max(1, rows / cols))); its other scaling,
+"match_rms_adamw", is not one the pages give and is refused.  The momentum
+state keeps PyTorch's name, ``momentum_buffer``.  (``nesterov`` defaults to
+False here, the pages' plain step; PyTorch defaults to True.)
 """
 from __future__ import annotations
 
@@ -26,7 +34,18 @@ class Muon(torch.optim.Optimizer):
     def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, ns_steps: int = 5,
                  adamw_lr: float = 1e-3, adamw_betas=(0.9, 0.95), adamw_eps: float = 1e-8,
                  wd: float = 0.01, coeffs=QUINTIC, rms_scale: str | None = None, eps: float = 1e-7,
-                 zero_centering: bool = False, nesterov: bool = False, ns_first: bool = False):
+                 zero_centering: bool = False, nesterov: bool = False, ns_first: bool = False,
+                 weight_decay: float | None = None, ns_coefficients=None,
+                 adjust_lr_fn: str | None = None):
+        if weight_decay is not None:
+            wd = weight_decay
+        if ns_coefficients is not None:
+            coeffs = tuple(ns_coefficients)
+        if adjust_lr_fn is not None:
+            if adjust_lr_fn != "original":
+                raise ValueError(f"adjust_lr_fn={adjust_lr_fn!r} is not supported; 'original' scales "
+                                 "the update by sqrt(max(1, rows / cols))")
+            rms_scale = "sqrt_max1"
         defaults = dict(lr=lr, momentum=momentum, ns_steps=ns_steps, adamw_lr=adamw_lr,
                         adamw_betas=tuple(adamw_betas), adamw_eps=adamw_eps, wd=wd, coeffs=coeffs,
                         rms_scale=rms_scale, eps=eps, zero_centering=zero_centering,
