@@ -75,3 +75,36 @@ def test_optimizer_group_variants_match_oracle(variant):
         got = p.detach().cpu().numpy() - h.param.astype(np.float64) * (1.0 - lr * wd)
         want = out["p"] - h.param.astype(np.float64) * (1.0 - lr * wd)
         assert rel(got, want) <= 2e-2
+
+
+@pytest.mark.skipif(not hasattr(torch.optim, "Muon"), reason="torch.optim.Muon missing")
+def test_drop_in_for_torch_optim_muon():
+    """The same two steps through this optimizer (on the GPU) and through
+    PyTorch's ``torch.optim.Muon`` (on the CPU), constructed with PyTorch's
+    keyword names: momentum buffers to 1e-5; the orthogonalised update to
+    4e-2 (each side is within 2e-2 of the exact step: bf16 iterations with
+    fp32 accumulation here, all-bf16 arithmetic in PyTorch's)."""
+    kw = dict(lr=0.02, momentum=0.95, weight_decay=0.01, nesterov=True, adjust_lr_fn="original")
+    shapes = [(256, 768), (768, 256), (1100, 1030)]
+    rng = np.random.default_rng(77)
+    p0 = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    ours = [torch.nn.Parameter(torch.from_numpy(p).to(DEV)) for p in p0]
+    ref = [torch.nn.Parameter(torch.from_numpy(p.copy())) for p in p0]
+    opt_ours, opt_ref = Muon(ours, **kw), torch.optim.Muon(ref, **kw)
+    for _ in range(2):
+        before_a = [p.detach().cpu().numpy().astype(np.float64) for p in ours]
+        before_b = [p.detach().numpy().astype(np.float64) for p in ref]
+        for a, b, s in zip(ours, ref, shapes):
+            g = rng.standard_normal(s).astype(np.float32)
+            a.grad = torch.from_numpy(g).to(DEV)
+            b.grad = torch.from_numpy(g)
+        opt_ours.step()
+        opt_ref.step()
+        torch.cuda.synchronize()
+        for a, b, pa, pb in zip(ours, ref, before_a, before_b):
+            ma = opt_ours.state[a]["momentum_buffer"].cpu().numpy()
+            mb = opt_ref.state[b]["momentum_buffer"].numpy()
+            assert rel(ma, mb) <= 1e-5
+            da = a.detach().cpu().numpy() - pa * (1 - 0.02 * 0.01)
+            db = b.detach().numpy() - pb * (1 - 0.02 * 0.01)
+            assert rel(da, db) <= 4e-2
