@@ -48,6 +48,8 @@ def kernel_sources_hash(phase: str | None = None) -> str:
 
 
 def _short(name: str) -> str:
+    """Kernel name without return type, namespaces and argument list."""
+    name = name.replace("(anonymous namespace)::", "")
     name = re.sub(r"^void\s+", "", name.split("(")[0])
     return name.replace("muon::", "")
 

@@ -62,3 +62,11 @@ def test_per_kernel_stamps(tmp_path, monkeypatch):
     assert "muon_gemm.h" in profiling.SOURCES_OF["x_update"]
     monkeypatch.setattr(profiling, "TRAFFIC_PROFILE", _profile(tmp_path, {"x_update": "0" * 16}, 7))
     assert profiling.current_traffic("x_update") is None
+
+
+def test_kernel_names_are_shortened_past_anonymous_namespaces():
+    from matrix_aware_optimizer_libmuon_amd.profiling import _short
+    assert _short("void muon::(anonymous namespace)::k_ns_fused<64>(muon::MatDesc const*, "
+                  "float const*, int, int)") == "k_ns_fused<64>"
+    assert _short("void muon::k_gram<256>(muon::MatDesc const*, long const*, int, long, int)") \
+        == "k_gram<256>"
