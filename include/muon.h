@@ -194,7 +194,8 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats,
  * launches kernels: no host staging, no allocation, no synchronisation, so it
  * may be captured into a HIP graph and replayed.
  *   muon_plan_create  arguments as muon_step_ex (same errors, found before
- *       anything is launched); *plan receives a host object the caller frees
+ *       anything is launched; MUON_EHIP also when the host object cannot be
+ *       allocated); *plan receives a host object the caller frees
  *       with muon_plan_destroy.  The param, grad and momentum pointers and the
  *       workspace are recorded: they must stay valid, and the workspace must
  *       not be used by other calls, while the plan lives.  New gradients are

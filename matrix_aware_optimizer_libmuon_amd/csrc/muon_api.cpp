@@ -704,7 +704,7 @@ int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
   if (!out) return MUON_EINVAL;
   *out = nullptr;
   std::unique_ptr<muon_plan> p(new (std::nothrow) muon_plan());
-  if (!p) return MUON_EINVAL;
+  if (!p) return hip_fail(hipErrorOutOfMemory, "host allocation of the plan");
   int rc = prepare_step(mats, n_mats, 0.f, 0.f, 0.f, ns_steps, coeffs, n_coeffs, rms_scale_mode,
                         eps, options, workspace, workspace_bytes, p->plan, p->t);
   if (rc != MUON_OK) return rc;
