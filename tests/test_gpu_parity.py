@@ -253,3 +253,31 @@ def test_graph_capture_is_refused_before_anything_runs():
     torch.cuda.synchronize()
     assert err is not None and err.status == muon.MUON_ECAPTURE
     assert np.array_equal(p.cpu().numpy(), mi.param) and np.array_equal(m.cpu().numpy(), mi.mom)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fp32_stages_at_kernel_level(dtype):
+    """The three HBM passes on their own, tighter than the step's 1e-5, over
+    every kernel class (fused, 128- and 256-tile) with a warm momentum:
+      K1  momentum mu M + (1 - mu) G and its norm, 1e-6 relative to fp64;
+      K2  X0 (the first bf16 iterate, read from the workspace after one
+          iteration) is the round-to-nearest of M / (nu + eps), taken from the
+          library's own M and nu: within half a bf16 ulp of the fp64 quotient;
+      K5  p (1 - lr wd) - lr s O for the library's own O, 1e-6."""
+    lr, mu, wd = 0.03, 0.9, 0.05
+    shapes = [(40, 300), (300, 100), (640, 200), (1100, 1030)]
+    inputs = [W.adhoc_inputs(r, c, dtype, seed=900 + k, mom_std=0.5) for k, (r, c) in enumerate(shapes)]
+    run = Run(inputs).step(lr=lr, mu=mu, wd=wd, ns_steps=1, rms_scale="sqrt_max1")
+    for i, mi in enumerate(inputs):
+        want_m = mu * mi.mom.astype(np.float64) + (1 - mu) * mi.grad.astype(np.float64)
+        e_m = rel(run.mom(i), want_m)
+        m_lib = run.mom(i).astype(np.float64)
+        e_nu = abs(run.nu(i) - np.linalg.norm(m_lib)) / np.linalg.norm(m_lib)
+        x = m_lib / (run.nu(i) + 1e-7)
+        got = run.x(i, 0)[:mi.rows, :mi.cols].astype(np.float64)
+        half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 8)
+        ok_x = np.all(np.abs(got - x) <= half_ulp * (1 + 2.0 ** -12) + 1e-38)
+        s = math.sqrt(max(1.0, mi.rows / mi.cols))
+        e_p = check_apply_consistency(run, i, lr, wd, s, tol=1e-6)
+        say(f"  {mi.rows}x{mi.cols} {dtype}: M {e_m:.1e} nu {e_nu:.1e} X0 RNE {ok_x} apply {e_p:.1e}")
+        assert e_m <= 1e-6 and e_nu <= 1e-6 and ok_x
