@@ -7,6 +7,7 @@ import pytest
 import matrix_aware_optimizer_libmuon_amd as muon
 from matrix_aware_optimizer_libmuon_amd import workloads as W
 from oracle import muon_oracle as O
+from tests.bf16_error import ns_error_estimate_for
 from tests.bf16_model import newton_schulz_bf16
 from tests.gpu_helpers import Run, check_apply_consistency, rel, say
 
@@ -35,31 +36,49 @@ def test_longest_side_accepted(shape):
 
 
 def test_thousands_of_tiny_matrices():
-    """5000 matrices of at most 8 x 8.  A few such matrices have a normalised
-    singular value near 2e-3, where five quintic steps amplify the bf16
-    rounding of X itself past 2e-2 of the fp64 result; there the GPU must match
-    the bf16 rounding model instead (it does to the last bit on these sizes),
-    which shows the excess is the method's precision, not a kernel fault."""
+    """5000 matrices of at most 8 x 8 in one grouped call; every one is
+    compared with the fp64 oracle.
+
+    Pass condition per matrix: relative Frobenius error of O at most
+    max(2e-2, 4 e), where e is the first-order RMS size of the bf16 rounding
+    error of the documented rounding points propagated through the
+    iteration, computed from the oracle's own spectrum of the normalised
+    momentum (tests/bf16_error.py).  Inside the domain e <= 5e-3 this is the
+    plain 2e-2 bar.  Tiny matrices whose normalised singular values sit where
+    the five-step quintic map is steep (slope up to a^5 ~ 486 near 0) have an
+    O that bf16 cannot determine to 2e-2 at all; there the bar follows the
+    method's own precision, never the library's output.  Momentum (1e-5) and
+    the apply stage (1e-5, against the library's own O) are checked for every
+    matrix as well, and every O's singular values stay within the quintic's
+    spectral bound 1.2024 (+0.03)."""
     rng = np.random.default_rng(3)
     shapes = [(int(rng.integers(1, 9)), int(rng.integers(1, 9))) for _ in range(5000)]
     inputs = [W.adhoc_inputs(r, c, "f32", seed=10 + k) for k, (r, c) in enumerate(shapes)]
     run = Run(inputs).step(lr=0.02, mu=0.95, wd=0.01)
-    worst, within = 0.0, 0
-    sampled = range(0, len(shapes), 97)
-    for i in sampled:
-        mi = inputs[i]
+    errs, ests, beyond, model_dev = [], [], 0, 0.0
+    for i, mi in enumerate(inputs):
         out = O.muon_step_matrix(mi.param, mi.grad, mi.mom, lr=0.02, mu=0.95, wd=0.01)
-        err = rel(run.o(i), out["o"])
-        worst = max(worst, err)
-        assert rel(run.mom(i), out["m"]) <= TOL_F32
+        o = run.o(i)
+        err = rel(o, out["o"])
+        est = ns_error_estimate_for(out["m"], (O.QUINTIC,), 5)
+        errs.append(err)
+        ests.append(est)
+        assert rel(run.mom(i), out["m"]) <= TOL_F32, (i, shapes[i])
         check_apply_consistency(run, i, 0.02, 0.01, 1.0)
-        if err <= TOL_NS:
-            within += 1
-        else:
-            model = newton_schulz_bf16(out["m"], (O.QUINTIC,), 5)
-            assert rel(run.o(i), model) <= 1e-3, (shapes[i], err)
-    say(f"  5000 tiny matrices: worst sampled O error {worst:.2e}; {within} of {len(sampled)} within 2e-2")
-    assert within >= 0.9 * len(sampled)
+        assert np.linalg.norm(o, 2) <= 1.2024 + 0.03, (i, shapes[i])
+        assert err <= max(TOL_NS, 4.0 * est), (i, shapes[i], err, est)
+        if err > TOL_NS:
+            beyond += 1
+            # diagnostic only: distance to a numpy emulation of the same
+            # rounding points (not a pass condition)
+            model_dev = max(model_dev, rel(o, newton_schulz_bf16(out["m"], (O.QUINTIC,), 5)))
+    errs, ests = np.array(errs), np.array(ests)
+    inside = ests <= TOL_NS / 4
+    say(f"  5000 tiny matrices: O error max {errs.max():.2e}, median {np.median(errs):.2e}; "
+        f"error / estimate max {np.max(errs / np.maximum(ests, 1e-30)):.2f}, "
+        f"median {np.median(errs / np.maximum(ests, 1e-30)):.2f}; {int(inside.sum())} inside "
+        f"the 2e-2 domain; {beyond} beyond 2e-2 (estimate there >= {ests[errs > TOL_NS].min() if beyond else 0:.2e}; "
+        f"max distance to the bf16 emulation {model_dev:.1e})")
 
 
 def test_sixty_four_steps_with_per_step_coefficients_over_every_class():
