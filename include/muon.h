@@ -55,6 +55,14 @@
  * Thread safety: calls may come from several host threads; two calls that
  * run concurrently must use different workspaces.
  *
+ * Debugging: with MUON_DEBUG set in the environment (any value but "0"),
+ * every call keeps all its launches on the caller's stream, synchronises and
+ * checks for an error after each launch (MUON_EHIP names the phase), and
+ * fills the workspace's iteration buffers with bf16 NaN before a step, so a
+ * kernel that read a value no kernel of the step wrote would leave NaN in the
+ * result.  The variable is read at every call.  Not for production: it
+ * serialises the host with the device.
+ *
  * Graph capture: every call stages its descriptor table through a small ring
  * of pinned host buffers that later calls reuse, so a captured copy would
  * replay stale tables.  A call on a stream that is capturing returns

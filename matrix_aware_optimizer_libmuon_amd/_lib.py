@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmuon.so")
+# MUON_LIB selects another build of the same library (e.g. the host
+# AddressSanitizer build of build.py --asan); the default is the in-place one.
+LIB_PATH = os.environ.get("MUON_LIB") or os.path.join(_HERE, "libmuon.so")
 
 MUON_OK = 0
 MUON_EINVAL = -1

@@ -2,6 +2,14 @@
 marshalling module (_marshal, plain C++ against torch's headers, g++).
 
     python -m matrix_aware_optimizer_libmuon_amd.build
+    python -m matrix_aware_optimizer_libmuon_amd.build --asan OUT_DIR
+
+The second form builds a copy of the library whose host code (argument
+checks, workspace planning, descriptor tables, the staging ring) is compiled
+with AddressSanitizer; the device code is the same.  Load it by pointing
+MUON_LIB at OUT_DIR/libmuon.so, with the sanitizer runtime (asan_runtime())
+preloaded into a process that is not itself instrumented, e.g. Python:
+    LD_PRELOAD=<asan_runtime()> ASAN_OPTIONS=detect_leaks=0 MUON_LIB=... python ...
 """
 from __future__ import annotations
 
@@ -99,5 +107,41 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str | None:
+    """Path of the clang AddressSanitizer runtime of the ROCm toolchain."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_asan(out_dir: str, verbose: bool = False) -> str:
+    """libmuon.so in out_dir with the host dispatcher under AddressSanitizer
+    (hipcc: -Xarch_host before the sanitizer flag keeps it off the device
+    code).  The kernel objects are compiled as usual."""
+    os.makedirs(out_dir, exist_ok=True)
+    jobs, objs = [], []
+    for src, extra in SOURCES:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        if src == "muon_api.cpp":
+            extra = [*extra, "-Xarch_host", "-fsanitize=address", "-fno-omit-frame-pointer", "-g"]
+        jobs.append(_start([HIPCC, *FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], verbose))
+        objs.append(obj)
+    try:
+        for job in jobs:
+            _finish(job, verbose)
+    finally:
+        for _, proc in jobs:
+            if proc.poll() is None:
+                proc.kill()
+                proc.wait()
+    out = os.path.join(out_dir, "libmuon.so")
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan",
+          "-Xarch_host", "-fsanitize=address", "-o", out, *objs], verbose)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(sys.argv[sys.argv.index("--asan") + 1], verbose="-q" not in sys.argv))
+    else:
+        print(build(verbose="-q" not in sys.argv))

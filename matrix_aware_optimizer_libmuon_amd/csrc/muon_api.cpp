@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -73,6 +75,7 @@ struct Plan {
   size_t desc_off = 0, prefix_off[kNumPrefix] = {}, nrm2_off = 0, coeff_off = 0, table_bytes = 0;
   size_t colsum_off = 0;
   int64_t colsum_count = 0;           // doubles in the column-sum region
+  size_t buf_off = 0;                 // start of the per-matrix X / A / C buffers
   size_t total = 0;
   std::vector<MatPlan> mats;
 };
@@ -107,6 +110,7 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
     plan.colsum_count += c;
   }
   off = align_up(plan.colsum_off + static_cast<size_t>(plan.colsum_count) * sizeof(double), kAlign);
+  plan.buf_off = off;
   for (int64_t i = 0; i < n; ++i) {
     MatPlan& m = plan.mats[static_cast<size_t>(i)];
     const int64_t r = m.rows, c = m.cols;
@@ -140,7 +144,11 @@ bool make_plan(int64_t n, GetShape shape, Plan& plan) {
 // ---------------------------------------------------------------------------
 // pinned staging ring for the descriptor upload (per device)
 // ---------------------------------------------------------------------------
+// Each slot has its own lock: a call waits only for the copy that last used
+// the slot it takes (eight calls back), never while holding the library-wide
+// lock, so calls on other devices and other slots go on meanwhile.
 struct Slot {
+  std::mutex mu;
   void* host = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
@@ -151,11 +159,33 @@ constexpr int kSlots = 8;
 
 struct DeviceState {
   Slot slots[kSlots];
-  int next = 0;
+  std::atomic<unsigned> next{0};
 };
 
-std::mutex g_mu;
-std::map<int, DeviceState> g_dev;
+std::mutex g_mu;                       // guards the maps below and the timing record
+std::map<int, DeviceState> g_dev;      // node-based: references stay valid
+
+DeviceState& device_state(int dev) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return g_dev[dev];
+}
+
+// MUON_DEBUG (environment, read at every call; any value but "" or "0"):
+// every launch stays on the caller's stream and is followed by a
+// synchronisation and an error check that names the phase, and before a step
+// the workspace's iteration buffers (X, A, C of every matrix) are filled with
+// bf16 NaN, so that a kernel reading a value that no kernel of the step wrote
+// turns the result into NaN.  For debugging only: it serialises the host with
+// the device.
+thread_local bool g_debug = false;
+bool debug_env() {
+  const char* v = std::getenv("MUON_DEBUG");
+  return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+constexpr uint32_t kBf16NanPair = 0x7FC07FC0u;
+const char* const kPhaseName[kNumPhases] = {"momentum+norm", "normalise+cast", "Gram X X^T",
+                                            "C = aI + bA + cA^2", "X update", "apply",
+                                            "AdamW", "fused iteration"};
 
 // timing
 struct TimingRec {
@@ -178,8 +208,8 @@ hipEvent_t pool_event() {
   return e;
 }
 
-int hip_fail(hipError_t e, const char* what) {
-  g_hip_detail = std::string(what) + ": " + hipGetErrorString(e);
+int hip_fail(hipError_t e, const std::string& what) {
+  g_hip_detail = what + ": " + hipGetErrorString(e);
   return MUON_EHIP;
 }
 
@@ -203,10 +233,9 @@ int upload_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
   if (cap != hipStreamCaptureStatusNone) return MUON_ECAPTURE;
   if (!stream_on_device(stream, dev)) return MUON_EINVAL;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceState& st = g_dev[dev];
-  Slot& s = st.slots[st.next];
-  st.next = (st.next + 1) % kSlots;
+  DeviceState& st = device_state(dev);
+  Slot& s = st.slots[st.next.fetch_add(1, std::memory_order_relaxed) % kSlots];
+  std::lock_guard<std::mutex> lock(s.mu);
   if (s.pending) {
     // wait for the copy that last used this slot (polled: a blocking wait
     // may put the thread to sleep for longer than a small step takes)
@@ -326,7 +355,22 @@ int timed(int phase, hipStream_t stream, F&& launch) {
     std::lock_guard<std::mutex> lock(g_mu);
     g_trecs.push_back({phase, a, b});
   }
+  if (g_debug && !g_no_timing) {   // (never while the stream is capturing)
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess)
+      return hip_fail(e, std::string("MUON_DEBUG check after the ") + kPhaseName[phase] + " launch");
+  }
   return MUON_OK;
+}
+
+// MUON_DEBUG: NaN over every matrix's X / A / C buffers before a step.
+int debug_poison(const Plan& plan, char* ws, hipStream_t stream) {
+  if (!g_debug || g_no_timing || plan.total <= plan.buf_off) return MUON_OK;
+  const int err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws + plan.buf_off),
+                                  static_cast<int64_t>((plan.total - plan.buf_off) / 4), kBf16NanPair,
+                                  static_cast<void*>(stream));
+  return err == hipSuccess ? MUON_OK : hip_fail(static_cast<hipError_t>(err), "MUON_DEBUG fill");
 }
 
 struct Table {
@@ -507,7 +551,7 @@ int launch_all(const Plan& plan, const Table& t, char* ws, bool ortho, float lr,
     std::lock_guard<std::mutex> lock(g_mu);
     timing = g_timing && !g_no_timing;
   }
-  const bool fork = side && !timing && nf > 0 && ns_steps > 0 && (nb + ns) > 0;
+  const bool fork = side && !timing && !g_debug && nf > 0 && ns_steps > 0 && (nb + ns) > 0;
   hipStream_t fs = fork ? side->stream : stream;
   if (fork) {
     rc = stream_after(*side, side->fork, fs, stream);
@@ -572,6 +616,8 @@ int run_sequence(const Plan& plan, Table& t, char* ws, bool ortho, float lr, flo
                  hipStream_t stream) {
   fill_coeffs(plan, t, ns_steps, coeffs, n_coeffs);
   int rc = upload_table(t.bytes.data(), t.bytes.size(), ws, stream);
+  if (rc != MUON_OK) return rc;
+  rc = debug_poison(plan, ws, stream);
   if (rc != MUON_OK) return rc;
   SidePair* side = nullptr;
   if (wants_side(t, ns_steps)) {
@@ -681,6 +727,7 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
                  int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode,
                  float eps, const muon_options_t* options, void* workspace, size_t workspace_bytes,
                  hipStream_t stream) {
+  g_debug = debug_env();
   Plan plan;
   Table t;
   const int rc = prepare_step(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs,
@@ -743,7 +790,10 @@ int muon_plan_step(const muon_plan_t* plan, const float* hyper, hipStream_t stre
   // events recorded inside a graph cannot be read back: no phase timing then
   g_no_timing = cap != hipStreamCaptureStatusNone;
   char* ws = plan->ws;
-  int rc = timed(kPhaseMomentumNorm, stream, [&] {
+  g_debug = debug_env();
+  int rc = debug_poison(plan->plan, ws, stream);
+  if (rc == MUON_OK)
+    rc = timed(kPhaseMomentumNorm, stream, [&] {
     return launch_fill_zero(reinterpret_cast<double*>(ws + plan->plan.nrm2_off), plan->plan.n,
                             static_cast<void*>(stream));
   });
@@ -760,6 +810,7 @@ void muon_plan_destroy(muon_plan_t* plan) { delete plan; }
 int muon_orthogonalize(const muon_ortho_t* mats, int64_t n_mats, int ns_steps,
                        const muon_ns_coeff_t* coeffs, int n_coeffs, float eps, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
+  g_debug = debug_env();
   if (n_mats < 0 || (n_mats > 0 && !mats)) return MUON_EINVAL;
   if (n_mats > (int64_t(1) << 24)) return MUON_EINVAL;
   int rc = check_common(ns_steps, coeffs, n_coeffs, eps);
@@ -833,6 +884,7 @@ size_t muon_adamw_workspace_bytes(int64_t n_tensors) {
 int muon_adamw_step(const muon_adamw_tensor_t* tensors, int64_t n_tensors, float lr, float beta1,
                     float beta2, float eps, float wd, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
+  g_debug = debug_env();
   if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return MUON_EINVAL;
   if (n_tensors > (int64_t(1) << 24)) return MUON_EINVAL;
   if (!finite(lr) || !finite(wd) || !finite(eps) || !(eps >= 0.0f)) return MUON_EINVAL;

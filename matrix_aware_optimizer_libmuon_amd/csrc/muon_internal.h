@@ -6,6 +6,7 @@
 // sum of all matrices' units: a workgroup finds its matrix by binary search
 // in the prefix array.
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 namespace muon {
@@ -112,6 +113,7 @@ int launch_momentum_norm(const MatDesc* d, const int64_t* prefix, int n, int64_t
 int launch_normalize(const MatDesc* d, const int64_t* prefix, int n, int64_t units,
                      float eps, float mu, const float* hyper, void* stream);
 int launch_fill_zero(double* p, int64_t count, void* stream);
+int launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, void* stream);
 int launch_colsum(const MatDesc* d, const int64_t* prefix, int n, int64_t units, double* zero_from,
                   int64_t zero_count, void* stream);
 // GEMM phases: `tile` is 128 or 256; every matrix of the launch is of that class

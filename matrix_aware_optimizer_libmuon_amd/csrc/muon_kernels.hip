@@ -191,6 +191,14 @@ __global__ __launch_bounds__(kEwThreads) void k_fill_zero_f64(double* p, int64_t
     p[k] = 0.0;
 }
 
+// Fill count 32-bit words with a value (the debug mode's NaN poisoning of the
+// iteration buffers; a kernel, not a memset node, so it is safe in any stream).
+__global__ __launch_bounds__(kEwThreads) void k_fill_u32(uint32_t* p, int64_t count, uint32_t value) {
+  for (int64_t k = blockIdx.x * static_cast<int64_t>(kEwThreads) + threadIdx.x; k < count;
+       k += static_cast<int64_t>(gridDim.x) * kEwThreads)
+    p[k] = value;
+}
+
 __global__ __launch_bounds__(kEwThreads) void k_colsum(const MatDesc* __restrict__ descs,
                                                        const int64_t* __restrict__ prefix, int n) {
   const int64_t unit = blockIdx.x;
@@ -479,6 +487,14 @@ int launch_fill_zero(double* p, int64_t count, void* stream) {
   const int64_t blocks = (count + kEwThreads - 1) / kEwThreads;
   hipLaunchKernelGGL(k_fill_zero_f64, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)),
                      dim3(kEwThreads), 0, static_cast<hipStream_t>(stream), p, count);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, void* stream) {
+  if (count <= 0) return 0;
+  const int64_t blocks = (count + kEwThreads - 1) / kEwThreads;
+  hipLaunchKernelGGL(k_fill_u32, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                     dim3(kEwThreads), 0, static_cast<hipStream_t>(stream), p, count, value);
   return static_cast<int>(hipGetLastError());
 }
 
