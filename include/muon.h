@@ -193,6 +193,32 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats,
                  int rms_scale_mode, float eps, const muon_options_t* options,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- a step that allocates nothing ---------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step as muon_step, with the workspace replaced by a fixed scratch array of
+ * MUON_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on, for the life of the process.  The caller still passes every parameter,
+ * gradient and momentum buffer.  The call allocates no device or pinned host
+ * memory and creates no stream or event: the descriptor table reaches the
+ * device in kernel arguments, and every launch stays on `stream` (no side
+ * stream; phase timing and MUON_DEBUG do not apply).
+ *   Arguments and errors as muon_step, plus MUON_EWORKSPACE when
+ *   muon_workspace_bytes(mats, n_mats) exceeds MUON_NOALLOC_SCRATCH_BYTES
+ *   (found before anything is launched; nothing is modified then).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (each call rewrites what it reads before reading it): two
+ * calls whose work overlaps on one device race, so order them on one stream
+ * or with events.  The intermediates of the last call are readable through
+ * muon_noalloc_scratch() at the offsets muon_workspace_view() gives. */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+int muon_step_noalloc(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd,
+                      int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs,
+                      int rms_scale_mode, float eps, hipStream_t stream);
+/* Device address of the current device's scratch array (for reading the last
+ * muon_step_noalloc call's intermediates); NULL if it cannot be resolved. */
+void* muon_noalloc_scratch(void);
+
 /* ---- a step prepared once over fixed buffers ----------------------------
  * The pages' optimizer steps the same parameters every iteration (the
  * Muon.step loop of airosetta.com; _step_muon of wmrh.cn section 4.2).  A plan

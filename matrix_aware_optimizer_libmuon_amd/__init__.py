@@ -159,6 +159,34 @@ def muon_step(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 
     return workspace
 
 
+# Bytes of the fixed per-device scratch of muon_step_noalloc (include/muon.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def muon_step_noalloc(params: Sequence, grads: Sequence, moms: Sequence, *, lr: float = 0.02,
+                      mu: float = 0.95, wd: float = 0.0, ns_steps: int = 5, coeffs=QUINTIC,
+                      rms_scale: str | None = None, eps: float = 1e-7,
+                      scales: Sequence | None = None, stream=None) -> None:
+    """muon_step without a workspace and without any allocation
+    (``muon_step_noalloc``): the intermediates live in the library's fixed
+    per-device scratch of NOALLOC_SCRATCH_BYTES, shared by every such call on
+    the device (calls that overlap on one device race)."""
+    torch = _torch()
+    n = len(params)
+    if rms_scale not in (None, "none", "sqrt_max1"):
+        raise ValueError(f"unknown rms_scale {rms_scale!r}")
+    mode = MUON_SCALE_SQRT_MAX1 if rms_scale == "sqrt_max1" else MUON_SCALE_NONE
+    arr = (MuonMatrix * max(1, n))()
+    sc = [] if scales is None else [0.0 if s is None else float(s) for s in scales]
+    _marshaller().fill_matrices(params, grads, moms, sc, ctypes.addressof(arr))
+    device = params[0].device if n else torch.device("cuda")
+    carr, nc = _coeff_array(coeffs, ns_steps)
+    with _on(device):
+        st = _lib.load().muon_step_noalloc(arr, n, float(lr), float(mu), float(wd), int(ns_steps),
+                                           carr, nc, mode, float(eps), _stream_handle(stream, device))
+    _lib.check(st, "muon_step_noalloc")
+
+
 class Plan:
     """A Muon step prepared once over fixed tensors (``muon_plan_create``):
     ``step()`` then only launches kernels, so it can be captured into a CUDA

@@ -39,7 +39,8 @@ EXPORTED = ("muon_workspace_bytes", "muon_step", "muon_step_ex", "muon_plan_crea
             "muon_plan_step", "muon_plan_destroy", "muon_orthogonalize",
             "muon_workspace_view",
             "muon_adamw_workspace_bytes", "muon_adamw_step",
-            "muon_timing_enable", "muon_timing_read", "muon_status_string", "muon_version")
+            "muon_timing_enable", "muon_timing_read", "muon_status_string", "muon_version",
+            "muon_step_noalloc", "muon_noalloc_scratch")
 
 
 class MuonMatrix(ctypes.Structure):
@@ -135,6 +136,12 @@ def load() -> ctypes.CDLL:
     lib.muon_timing_read.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_step_noalloc.argtypes = [P(MuonMatrix), ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, ctypes.c_int, P(MuonCoeff), ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    lib.muon_step_noalloc.restype = ctypes.c_int
+    lib.muon_noalloc_scratch.argtypes = []
+    lib.muon_noalloc_scratch.restype = ctypes.c_void_p
     lib.muon_version.argtypes = []
     lib.muon_version.restype = ctypes.c_char_p
     _lib = lib

@@ -744,6 +744,41 @@ int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, flo
                       nullptr, workspace, workspace_bytes, stream);
 }
 
+int muon_step_noalloc(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd,
+                      int ns_steps, const muon_ns_coeff_t* coeffs, int n_coeffs,
+                      int rms_scale_mode, float eps, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  e = static_cast<hipError_t>(noalloc_scratch(dev, &ws));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (scratch)");
+  Plan plan;
+  Table t;
+  // the scratch is checked like a caller's workspace of that size
+  int rc = prepare_step(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs, rms_scale_mode, eps,
+                        nullptr, ws, MUON_NOALLOC_SCRATCH_BYTES, plan, t);
+  if (rc != MUON_OK || t.n_active == 0) return rc;
+  if (!stream_on_device(stream, dev)) return MUON_EINVAL;
+  fill_coeffs(plan, t, ns_steps, coeffs, n_coeffs);
+  e = static_cast<hipError_t>(put_bytes(ws, t.bytes.data(), t.bytes.size(), static_cast<void*>(stream)));
+  if (e != hipSuccess) return hip_fail(e, "descriptor table (kernel arguments)");
+  // no side stream, no timing events, no debug checks: nothing is created
+  g_debug = false;
+  g_no_timing = true;
+  rc = launch_all(plan, t, static_cast<char*>(ws), false, lr, mu, wd, nullptr, ns_steps, coeffs,
+                  n_coeffs, eps, stream, nullptr);
+  g_no_timing = false;
+  return rc;
+}
+
+void* muon_noalloc_scratch(void) {
+  int dev = 0;
+  void* ws = nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || noalloc_scratch(dev, &ws) != hipSuccess) return nullptr;
+  return ws;
+}
+
 int muon_plan_create(const muon_matrix_t* mats, int64_t n_mats, int ns_steps,
                      const muon_ns_coeff_t* coeffs, int n_coeffs, int rms_scale_mode, float eps,
                      const muon_options_t* options, void* workspace, size_t workspace_bytes,

@@ -133,6 +133,12 @@ int launch_adamw(const AdamDesc* d, const int64_t* prefix, int n, int64_t units,
 int launch_ns_fused(int m_pad, const MatDesc* d, int n, const float* coeffs, int n_coeffs,
                     int ns_steps, int lds_bytes, void* stream);
 
+// fixed scratch of muon_step_noalloc (muon_noalloc.hip): the address of the
+// current device's array (resolved once per device), and a copy of host bytes
+// into device memory through kernel arguments (no staging buffer)
+int noalloc_scratch(int dev, void** out);
+int put_bytes(void* dst, const void* src, size_t bytes, void* stream);
+
 // per-tile GEMM launchers (muon_gemm256.hip, muon_gemm128.hip)
 int launch_gram_256(const MatDesc* d, const int64_t* prefix, int n, int64_t units, int parity,
                    void* stream);

@@ -28,7 +28,9 @@ _GEMM = _COMMON + ("muon_gemm.h", "muon_gemm256.hip", "muon_gemm128.hip")
 # the sources each bench phase's kernel is compiled from
 SOURCES_OF = {"momentum_norm": _ELEMENTWISE, "normalize_cast": _ELEMENTWISE, "apply": _ELEMENTWISE,
               "adamw": _ELEMENTWISE, "gram": _GEMM, "gram2_epilogue": _GEMM, "x_update": _GEMM,
-              "ns_fused": _COMMON + ("muon_fused.hip",)}
+              "ns_fused": _COMMON + ("muon_fused.hip",),
+              # the descriptor-table writer of the no-allocation step (no bench phase)
+              "noalloc_table": _COMMON + ("muon_noalloc.hip",)}
 KERNEL_SOURCES = tuple(sorted({f for files in SOURCES_OF.values() for f in files}))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "muon_step_transformer_d4096_hbm_traffic.md")
 
