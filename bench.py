@@ -4,11 +4,16 @@
 
 One step = one muon_step call over the whole workload (momentum + norm,
 normalise + cast, 5 x {Gram, Gram^2 epilogue, X update}, apply), with every
-input already resident in HBM.  Prints ONE JSON line:
+input already resident in HBM.  Timing: W untimed warm-up steps, then K timed
+steps, each bracketed by HIP events on the launch stream; before each step the
+momentum and parameter buffers are restored from a device copy (outside the
+events), so every repetition sees identical inputs.  The whole timed loop is
+bracketed by device synchronisations; its wall time (restores included) is
+reported too.  Prints ONE JSON line:
 
 * value: nominal Newton-Schulz TFLOP/s of the whole step, counting
-  4 m^2 n + 2 m^3 per iteration and matrix (m the short side) over the step's
-  wall time;
+  4 m^2 n + 2 m^3 per iteration and matrix (m the short side) over the
+  median step time;
 * matrices_per_s, NS-only TFLOP/s, fractions of the bf16 dense MFMA peak;
 * roofline: the dominant kernel's algorithmic work per launch over its
   average launch time (HIP events on the launch stream, inside the timed
@@ -73,6 +78,36 @@ def phase_work(w, muon):
             "x_update": ("mfma", xupd), "apply": ("hbm", b_apply), "ns_fused": ("mfma", fused)}
 
 
+def phase_issued(w, muon):
+    """MFMA work the tiled kernels actually issue per launch (padded shapes):
+    the symmetric phases compute only the upper-triangle tiles, t (t + 1) / 2
+    of a t x t tile grid, each 2 T^2 K flops; the X update every tile of the
+    padded matrix, twice where C is a hi/lo pair."""
+    gram = gram2 = xupd = 0
+    for r, c in w.shapes:
+        v = muon.workspace_view([(r, c)], 0, w.ns_steps)
+        t = v["tile"]
+        if t == FUSED_TILE:
+            continue
+        mp, npad = v["m_pad"], (v["rows_pad"] if v["transposed"] else v["cols_pad"])
+        k = mp // t
+        gram += k * (k + 1) // 2 * 2 * t * t * npad
+        gram2 += k * (k + 1) // 2 * 2 * t * t * mp
+        xupd += (2 if min(r, c) <= 128 else 1) * 2 * mp * mp * npad
+    return {"gram": gram, "gram2_epilogue": gram2, "x_update": xupd}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, target_s: float = 20.0):
     """The fp64 oracle on a bounded sample of the workload's matrices, timed
     on this host's cores.  Returns the dict of the JSON line."""
@@ -107,6 +142,7 @@ def cpu_baseline(w, target_s: float = 20.0):
     secs = sum(t for _, t in done)
     shapes = [f"{w.shapes[i][0]}x{w.shapes[i][1]}" for i, _ in done]
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus_visible": len(os.sched_getaffinity(0)),
             "seconds": secs, "matrices_per_s": len(done) / secs,
             "sample": f"{len(done)} matrices of the workload ({', '.join(shapes)}), one fp64 oracle "
                       f"step each (numpy, BLAS threads={cores}); input generation excluded"}
@@ -207,8 +243,8 @@ def bench_adamw(torch, muon, dev, reps: int = 10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -257,7 +293,19 @@ def main():
     kw = dict(lr=w.lr, mu=w.mu, wd=w.wd, ns_steps=w.ns_steps, coeffs=QUINTIC,
               rms_scale=w.rms_mode, eps=w.eps, workspace=ws, stream=stream)
 
+    # device copies of the state the step updates, restored before every step
+    p0 = [t.clone() for t in params]
+    m0 = [t.clone() for t in moms]
+    torch.cuda.synchronize()
+
+    def restore():
+        for t, src in zip(params, p0):
+            t.copy_(src)
+        for t, src in zip(moms, m0):
+            t.copy_(src)
+
     for k in range(args.warmup):
+        restore()
         muon.muon_step(params, grads, moms, **kw)
         torch.cuda.synchronize()
         log(f"[bench] warmup step {k + 1}/{args.warmup} done")
@@ -265,16 +313,25 @@ def main():
     if not args.no_phase_timing:
         muon.timing_enable(True)
         muon.timing_read()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
+        restore()
+        ev[k][0].record(stream)
         muon.muon_step(params, grads, moms, **kw)
+        ev[k][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     phases = muon.timing_read() if not args.no_phase_timing else None
     muon.timing_enable(False)
-    ms_per_step = elapsed * 1e3 / args.steps
-    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = float(np.median(step_ms))
+    log(f"[bench] {args.steps} timed steps: median {ms_per_step:.3f} ms/step "
+        f"(min {step_ms.min():.3f}, max {step_ms.max():.3f}; wall {elapsed * 1e3 / args.steps:.3f} "
+        f"ms/step with the state restores)")
+    del p0, m0
 
     flops_step = w.ns_flops()
     value = flops_step / (ms_per_step / 1e3) / 1e12
@@ -289,7 +346,12 @@ def main():
                       "eps": w.eps, "rms_scale": w.rms_mode},
            "matrices_per_s": w.n_mats / (ms_per_step / 1e3),
            "frac_of_bf16_peak": value / BF16_PEAK_TFLOPS,
-           "nominal_ns_flops_per_step": flops_step}
+           "nominal_ns_flops_per_step": flops_step,
+           "timing": {"ms_per_step": "median of the per-step HIP-event times",
+                      "step_ms_mean": float(step_ms.mean()), "step_ms_min": float(step_ms.min()),
+                      "step_ms_max": float(step_ms.max()),
+                      "wall_ms_per_step": elapsed * 1e3 / args.steps,
+                      "between_steps": "momentum and parameters restored from a device copy"}}
 
     if phases is not None:
         work = phase_work(w, muon)
@@ -312,6 +374,18 @@ def main():
                              "bound": "hbm", "achieved": achieved, "unit": "GB/s",
                              "peak": HBM_PEAK_GBS, "frac": achieved / HBM_PEAK_GBS,
                              "algorithmic_per_launch": amount}
+        # MFMA counters of the committed profile (null when the kernels
+        # changed since it was taken), and the rate on the work the
+        # symmetric kernels actually issue (upper-triangle tiles only)
+        from matrix_aware_optimizer_libmuon_amd.profiling import current_mfma
+        issued = phase_issued(w, muon)
+        for name in ("gram", "gram2_epilogue", "x_update"):
+            if name in per:
+                busy, _ = current_mfma(name)
+                per[name]["mfma_busy_per_cycle"] = busy
+                per[name]["issued_per_launch"] = issued[name]
+                per[name]["issued_frac"] = (issued[name] / (per[name]["avg_launch_ms"] / 1e3) / 1e12
+                                            / BF16_PEAK_TFLOPS)
         ns_ms = sum(phases[k]["ms"] for k in NS_PHASES) / args.steps
         out["ns_ms_per_step"] = ns_ms
         out["ns_tflops"] = flops_step / (ns_ms / 1e3) / 1e12
@@ -327,6 +401,8 @@ def main():
         out["roofline"] = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
                            "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
                            "traffic": d["traffic"]}
+        if "mfma_busy_per_cycle" in d:
+            out["roofline"]["mfma_busy_per_cycle"] = d["mfma_busy_per_cycle"]
 
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4

@@ -2,6 +2,13 @@
 
     python -m matrix_aware_optimizer_libmuon_amd.profiling trace  <kernel_stats.csv> <title> <command>
     python -m matrix_aware_optimizer_libmuon_amd.profiling traffic <fetch.csv> <write.csv> <title> <commands>
+    python -m matrix_aware_optimizer_libmuon_amd.profiling mfma <counters.csv> <kernel_trace.csv> <title> <command>
+
+The MFMA summary records, per Newton-Schulz GEMM kernel, the fraction of
+cycles the MFMA units were busy (rocprofv3's MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES
+over GRBM_GUI_ACTIVE times the SIMD count), the bf16 MFMA work issued
+(SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops) and the shader clock the kernel
+ran at, stamped like the traffic figures.
 
 The traffic summary records, per libmuon kernel, FETCH_SIZE and WRITE_SIZE
 (KiB per dispatch) scaled by what the same counters read for a plain device
@@ -33,6 +40,7 @@ SOURCES_OF = {"momentum_norm": _ELEMENTWISE, "normalize_cast": _ELEMENTWISE, "ap
               "noalloc_table": _COMMON + ("muon_noalloc.hip",)}
 KERNEL_SOURCES = tuple(sorted({f for files in SOURCES_OF.values() for f in files}))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "muon_step_transformer_d4096_hbm_traffic.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "muon_step_transformer_d4096_mfma_util.md")
 
 # kernel symbol -> bench phase name
 PHASE_OF = {"k_momentum_norm": "momentum_norm", "k_normalize": "normalize_cast",
@@ -105,18 +113,63 @@ def traffic_summary(fetch_csv: str, write_csv: str, title: str, commands: str,
     return "\n".join(out) + "\n"
 
 
-def current_traffic(phase: str):
-    """HBM bytes per launch of `phase` from the committed profile, or None when
-    there is none or the kernels changed since it was taken."""
+def mfma_summary(counters_csv: str, trace_csv: str, title: str, command: str) -> str:
+    """Per GEMM kernel: mean MfmaUtil (busy fraction), issued bf16 MFMA flops
+    per dispatch, GRBM_GUI_ACTIVE per dispatch (summed over the 8 XCDs by the
+    profiler, so divided by 8 here) and the clock that implies over the
+    kernel-trace duration of the same dispatches."""
+    util = _per_kernel_counter(counters_csv, "MfmaUtil")
+    mops = _per_kernel_counter(counters_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    gui = _per_kernel_counter(counters_csv, "GRBM_GUI_ACTIVE")
+    dur = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        dur[_short(r["Kernel_Name"])].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    out = [f"# {title}", "", "Command (repository root, one MI355X; counters in their own run):", "",
+           "```", command, "```", "",
+           "MfmaUtil is rocprofv3's derived metric: SQ_VALU_MFMA_BUSY_CYCLES summed over every SIMD, "
+           "over GRBM_GUI_ACTIVE (max over XCDs) times the SIMD count (1024). Issued flops are "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. The clock is GRBM_GUI_ACTIVE per XCD over the "
+           "dispatch's duration in the same run.", "",
+           "| kernel | MFMA busy / cycle | issued bf16 TFLOP / dispatch | GPU cycles / dispatch | "
+           "duration ms (profiled) | clock GHz |", "|---|---:|---:|---:|---:|---:|"]
+    busy, issued = {}, {}
+    for sym, phase in PHASE_OF.items():
+        if sym not in util or phase not in ("gram", "gram2_epilogue", "x_update"):
+            continue
+        cyc = gui.get(sym, 0.0) / 8.0
+        ms = sum(dur[sym]) / len(dur[sym]) / 1e6 if dur.get(sym) else float("nan")
+        ghz = cyc / (ms * 1e6) if ms == ms and ms > 0 else float("nan")
+        busy[phase] = util[sym] / 100.0
+        issued[phase] = mops.get(sym, 0.0) * 512
+        out.append(f"| `{sym}` | {busy[phase]:.3f} | {issued[phase] / 1e12:.2f} | {cyc:.4g} | "
+                   f"{ms:.3f} | {ghz:.2f} |")
+    out += ["", "Machine-readable (bench.py reports a kernel's figure only while the hash matches "
+            "the kernel sources):", "", "```json",
+            json.dumps({"kernel_sources_sha256_16": {k: kernel_sources_hash(k) for k in busy},
+                        "mfma_busy_per_cycle": {k: round(v, 4) for k, v in busy.items()},
+                        "issued_bf16_flops_per_dispatch": {k: round(v) for k, v in issued.items()}}),
+            "```"]
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel_counter(csv_path: str, counter: str) -> dict:
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            acc[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _stamped(path: str, key: str, phase: str):
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(path).read()
     except OSError:
         return None
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
         return None
     data = json.loads(m.group(1))
-    v = data.get("traffic_bytes_per_launch", {}).get(phase)
+    v = data.get(key, {}).get(phase)
     if v is None or phase not in SOURCES_OF:
         return None
     stamp = data.get("kernel_sources_sha256_16")
@@ -126,10 +179,25 @@ def current_traffic(phase: str):
     return float(v) if want == have else None
 
 
+def current_mfma(phase: str):
+    """(MFMA busy per cycle, issued bf16 flops per dispatch) of `phase` from the
+    committed counter profile; None entries when absent or stale."""
+    return (_stamped(MFMA_PROFILE, "mfma_busy_per_cycle", phase),
+            _stamped(MFMA_PROFILE, "issued_bf16_flops_per_dispatch", phase))
+
+
+def current_traffic(phase: str):
+    """HBM bytes per launch of `phase` from the committed profile, or None when
+    there is none or the kernels changed since it was taken."""
+    return _stamped(TRAFFIC_PROFILE, "traffic_bytes_per_launch", phase)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         sys.stdout.write(trace_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif sys.argv[1] == "traffic":
         sys.stdout.write(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
+    elif sys.argv[1] == "mfma":
+        sys.stdout.write(mfma_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
     else:
         raise SystemExit(__doc__)

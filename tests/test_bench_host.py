@@ -63,3 +63,18 @@ def test_cpu_baseline_leg_on_a_small_sample():
     assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
     assert out["value"] > 0 and out["cores"] >= 1 and out["seconds"] > 0
     assert "256x768" in out["sample"]
+
+
+def test_issued_work_of_the_symmetric_kernels():
+    """Upper-triangle tiles only: at m = 4096 with 256-tiles, 136 of the 256
+    tiles of the Gram and C products are issued (t (t + 1) / 2, t = 16); the X
+    update issues its full padded product."""
+    import bench
+    import matrix_aware_optimizer_libmuon_amd as muon
+    from matrix_aware_optimizer_libmuon_amd import workloads as W
+    w = W.WORKLOADS[3]
+    issued = bench.phase_issued(w, muon)
+    work = bench.phase_work(w, muon)
+    assert issued["gram"] / work["gram"][1] == pytest.approx(136 / 256)
+    assert issued["gram2_epilogue"] / work["gram2_epilogue"][1] == pytest.approx(136 / 256)
+    assert issued["x_update"] == work["x_update"][1]
