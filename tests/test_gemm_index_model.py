@@ -373,3 +373,49 @@ def test_c_epilogue_a_reads_are_bank_conflict_free():
                 for half in (slice(0, 32), slice(32, 64)):
                     b = banks[half].ravel()
                     assert len(np.unique(b)) == 64, (w, bi, bj)
+
+
+# ------------------------------------- rotated C-phase walk (never kept) ----
+def ring_schedule(kt_n, stages=4, ahead=3):
+    """gemm_tile's stage ring: (step whose data a load fetches, stage it lands
+    in, step in whose body it is issued) for the prologue and the loop, with
+    the clamp that makes loads past the end re-read the last step."""
+    ev = [(min(kt, kt_n - 1), kt % stages, -1) for kt in range(ahead)]
+    for kt in range(kt_n):
+        nxt = kt + ahead
+        ev.append((min(nxt, kt_n - 1), nxt % stages, kt))
+    return ev
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("m_pad_tiles", [1, 2, 3, 16])
+def test_rotated_c_walk_stays_in_bounds_and_in_ring_order(tile, m_pad_tiles):
+    """A C-phase K walk rotated to end on the A columns its epilogue reads
+    (start at krot = ((ti + 1) TILE / 32) mod kt_n, step kr = (kc + krot) mod
+    kt_n for the clamped step kc) reads every K step of A exactly once, from
+    inside A, for every upper tile (ti, tj); a stage is refilled only after
+    the step that last read it (same ring as the unrotated walk: the rotation
+    changes addresses, not the schedule); and the walk's last TILE / 32 steps
+    are the epilogue's columns.  (Index arithmetic of the walk as described;
+    the fault seen with that change is not explained by it.)"""
+    m_pad = m_pad_tiles * tile
+    kt_n = m_pad // BK
+    for ti in range(m_pad_tiles):
+        for tj in range(ti, m_pad_tiles):
+            krot = ((ti + 1) * tile // BK) % kt_n
+            seen = []
+            for kc, stage, issued_in in ring_schedule(kt_n):
+                kr = (kc + krot) % kt_n
+                for mn_layout in (False,):                  # C reads A K-contiguous
+                    for row0 in (ti * tile, tj * tile):
+                        mn, k, lds = dma_elements(tile, mn_layout, m_pad, row0, kr)
+                        assert mn.min() >= 0 and (mn * m_pad + k + 7).max() < m_pad * m_pad
+                        assert lds.min() >= 0 and (lds + 7).max() < tile * BK
+                # a load issued in step s refills stage (s + 3) % 4, last read in step s - 1
+                if issued_in >= 0:
+                    assert stage == (issued_in + 3) % 4 and (issued_in - 1) % 4 == stage
+                seen.append(kr)
+            walk = seen[:kt_n]                           # the steps the loop consumes
+            assert sorted(walk) == list(range(kt_n))
+            tail = walk[-(tile // BK):] if kt_n >= tile // BK else walk
+            assert sorted(tail) == list(range(ti * tile // BK, (ti + 1) * tile // BK))[-len(tail):]
