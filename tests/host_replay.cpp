@@ -1,0 +1,330 @@
+// Host-side replay of libmuon's dispatcher (muon_api.cpp, compiled unchanged
+// with the host C++ compiler) on the CPU: the HIP runtime calls it makes are
+// replaced by plain host stand-ins (a "device" buffer is host memory, a copy
+// is memcpy, streams and events are inert), and every kernel launcher records
+// its arguments instead of launching.  The checks then read the descriptor
+// table and prefix arrays the dispatcher really built, exactly as a kernel
+// would find them in the workspace:
+//   * the launch sequence: one launch per phase, the Gram / C / X-update
+//     triple per Newton-Schulz step and tile class, in order; the apply pass
+//     reads the iterate of parity ns_steps & 1; each C launch gets its step's
+//     coefficients;
+//   * each launch's unit count equals its prefix array's total, and each
+//     matrix owns t (t + 1) / 2 upper tiles (symmetric phases) or every tile
+//     (X update), with t = m_pad / tile;
+//   * every descriptor's workspace buffers (X0, X1, A, C, C_lo, norm slot,
+//     column sums) lie inside the workspace, 256-byte aligned where they are
+//     operands, sized for the padded shape, and disjoint across matrices;
+//     padding, orientation, split-C and vectorisation flags follow the shape;
+//     skipped matrices (no gradient) have no descriptor.
+// Usage: host_replay <case>; prints "ok" and exits 0, or the first failure.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "muon.h"
+#include "muon_internal.h"
+
+// ---------------------------------------------------------------- HIP ----
+extern "C" {
+hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* s) {
+  *s = hipStreamCaptureStatusNone;
+  return hipSuccess;
+}
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* d) { *d = 0; return hipSuccess; }
+hipError_t hipEventQuery(hipEvent_t) { return hipSuccess; }
+hipError_t hipEventCreate(hipEvent_t* e) { *e = reinterpret_cast<hipEvent_t>(new int(0)); return hipSuccess; }
+hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) { return hipEventCreate(e); }
+hipError_t hipEventDestroy(hipEvent_t e) { delete reinterpret_cast<int*>(e); return hipSuccess; }
+hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) { *ms = 0.f; return hipSuccess; }
+hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
+const char* hipGetErrorString(hipError_t) { return "replay"; }
+hipError_t hipGetLastError(void) { return hipSuccess; }
+hipError_t hipHostMalloc(void** p, size_t n, unsigned int) {
+  *p = std::malloc(n);
+  return *p ? hipSuccess : hipErrorOutOfMemory;
+}
+hipError_t hipHostFree(void* p) { std::free(p); return hipSuccess; }
+hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind, hipStream_t) {
+  std::memcpy(dst, src, n);
+  return hipSuccess;
+}
+hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned) {
+  *s = reinterpret_cast<hipStream_t>(new int(0));
+  return hipSuccess;
+}
+hipError_t hipStreamDestroy(hipStream_t s) { delete reinterpret_cast<int*>(s); return hipSuccess; }
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) { return hipSuccess; }
+}
+
+// ---------------------------------------------------------- launchers ----
+namespace muon {
+struct Launch {
+  std::string phase;
+  int tile = 0;
+  const MatDesc* d = nullptr;
+  const int64_t* prefix = nullptr;
+  int n = 0;
+  int64_t units = 0;
+  int parity = -1;
+  float a = 0, b = 0, c = 0;
+};
+std::vector<Launch> g_log;
+
+static int rec(const char* phase, int tile, const MatDesc* d, const int64_t* prefix, int n,
+               int64_t units, int parity = -1, float a = 0, float b = 0, float c = 0) {
+  Launch l;
+  l.phase = phase; l.tile = tile; l.d = d; l.prefix = prefix; l.n = n; l.units = units;
+  l.parity = parity; l.a = a; l.b = b; l.c = c;
+  g_log.push_back(l);
+  return 0;
+}
+int launch_momentum_norm(const MatDesc* d, const int64_t* p, int n, int64_t u, float, const float*, int, void*) {
+  return rec("momentum", 0, d, p, n, u);
+}
+int launch_normalize(const MatDesc* d, const int64_t* p, int n, int64_t u, float, float, const float*, void*) {
+  return rec("normalize", 0, d, p, n, u);
+}
+int launch_fill_zero(double*, int64_t, void*) { return rec("fill", 0, nullptr, nullptr, 0, 0); }
+int launch_fill_u32(uint32_t*, int64_t, uint32_t, void*) { return rec("poison", 0, nullptr, nullptr, 0, 0); }
+int launch_colsum(const MatDesc* d, const int64_t* p, int n, int64_t u, double*, int64_t, void*) {
+  return rec("colsum", 0, d, p, n, u);
+}
+int launch_gram(int tile, const MatDesc* d, const int64_t* p, int n, int64_t u, int parity, void*) {
+  return rec("gram", tile, d, p, n, u, parity);
+}
+int launch_gram2(int tile, const MatDesc* d, const int64_t* p, int n, int64_t u, float a, float b, float c, void*) {
+  return rec("gram2", tile, d, p, n, u, -1, a, b, c);
+}
+int launch_xupdate(int tile, const MatDesc* d, const int64_t* p, int n, int64_t u, int parity, void*) {
+  return rec("xupdate", tile, d, p, n, u, parity);
+}
+int launch_apply(const MatDesc* d, const int64_t* p, int n, int64_t u, int parity, float, float, float,
+                 const float*, int, void*) {
+  return rec("apply", 0, d, p, n, u, parity);
+}
+int launch_adamw(const AdamDesc*, const int64_t*, int, int64_t, float, float, float, void*) {
+  return rec("adamw", 0, nullptr, nullptr, 0, 0);
+}
+int launch_ns_fused(int m_pad, const MatDesc* d, int n, const float*, int, int, int, void*) {
+  return rec("fused", m_pad, d, nullptr, n, n);
+}
+int noalloc_scratch(int, void**) { return static_cast<int>(hipErrorNotSupported); }
+int put_bytes(void*, const void*, size_t, void*) { return static_cast<int>(hipErrorNotSupported); }
+}  // namespace muon
+
+// ------------------------------------------------------------- checks ----
+using namespace muon;
+static int g_fail = 0;
+#define CHECK(cond, ...)                                     \
+  do {                                                       \
+    if (!(cond)) {                                           \
+      if (g_fail++ < 10) {                                   \
+        std::printf("FAIL %s:%d: %s: ", __FILE__, __LINE__, #cond); \
+        std::printf(__VA_ARGS__);                            \
+        std::printf("\n");                                   \
+      }                                                      \
+    }                                                        \
+  } while (0)
+
+static int64_t ceil_to(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Case {
+  std::vector<std::pair<int64_t, int64_t>> shapes;
+  std::vector<bool> present;
+  int ns = 5;
+  std::vector<muon_ns_coeff_t> coeffs{{3.4445f, -4.7750f, 2.0315f}};
+};
+
+static void run_case(const char* name, const Case& cs) {
+  const int64_t n = static_cast<int64_t>(cs.shapes.size());
+  std::vector<muon_matrix_t> mats(n);
+  for (int64_t i = 0; i < n; ++i) {
+    muon_matrix_t& m = mats[i];
+    m.rows = cs.shapes[i].first;
+    m.cols = cs.shapes[i].second;
+    m.grad_dtype = MUON_BF16;
+    m.scale = 0.f;
+    // caller buffers: distinct, 16-byte aligned addresses (never dereferenced)
+    const uintptr_t base = 0x100000000000ull + static_cast<uintptr_t>(i) * 0x100000000ull;
+    m.param = reinterpret_cast<float*>(base);
+    m.momentum = reinterpret_cast<float*>(base + 0x40000000ull);
+    m.grad = cs.present.empty() || cs.present[i] ? reinterpret_cast<void*>(base + 0x80000000ull) : nullptr;
+  }
+  const size_t ws_bytes = muon_workspace_bytes(mats.data(), n);
+  CHECK(ws_bytes > 0, "%s: workspace size", name);
+  // the workspace: host memory standing in for device memory (untouched pages stay virtual)
+  char* raw = static_cast<char*>(std::malloc(ws_bytes + 256));
+  char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(raw) + 255) & ~uintptr_t(255));
+  g_log.clear();
+  const int rc = muon_step(mats.data(), n, 0.02f, 0.95f, 0.01f, cs.ns, cs.coeffs.data(),
+                           static_cast<int>(cs.coeffs.size()), MUON_SCALE_NONE, 1e-7f, ws, ws_bytes,
+                           nullptr);
+  CHECK(rc == MUON_OK, "%s: muon_step returned %d", name, rc);
+  if (rc != MUON_OK) { std::free(raw); return; }
+
+  // expected classes, from the shapes alone (the kernels' class rules)
+  auto fused = [](int64_t r, int64_t c) {
+    const int64_t m = ceil_to(std::min(r, c), kTileFused), nn = ceil_to(std::max(r, c), kTileFused);
+    return m <= kFusedMaxM && 2 * (m * ceil_to(nn, 128) + 2 * m * ceil_to(m, 128)) <= kFusedLdsMax;
+  };
+  auto tile_of = [&](int64_t r, int64_t c) {
+    return std::min(r, c) >= kBigMinM ? kTileBig : (fused(r, c) ? kTileFused : kTileSmall);
+  };
+  int n_active = 0, n_big = 0, n_small = 0, n_fused = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (!mats[i].grad) continue;
+    ++n_active;
+    const int t = tile_of(mats[i].rows, mats[i].cols);
+    (t == kTileBig ? n_big : t == kTileSmall ? n_small : n_fused) += 1;
+  }
+
+  // the launch sequence
+  std::vector<std::string> want{"momentum", "normalize"};
+  int fused_launches = 0;
+  for (const Launch& l : g_log) fused_launches += l.phase == "fused";
+  for (int f = 0; f < fused_launches; ++f) want.push_back("fused");
+  for (int k = 0; k < ((n_big + n_small) ? cs.ns : 0); ++k)
+    for (const char* ph : {"gram", "gram2", "xupdate"}) {
+      if (n_big) want.push_back(ph);
+      if (n_small) want.push_back(ph);
+    }
+  want.push_back("apply");
+  CHECK(g_log.size() == want.size(), "%s: %zu launches, want %zu", name, g_log.size(), want.size());
+  for (size_t k = 0; k < std::min(g_log.size(), want.size()); ++k)
+    CHECK(g_log[k].phase == want[k], "%s: launch %zu is %s, want %s", name, k, g_log[k].phase.c_str(),
+          want[k].c_str());
+  CHECK(!(n_fused && !fused_launches && cs.ns > 0), "%s: fused matrices but no fused launch", name);
+
+  // descriptors, read from the table the dispatcher uploaded into the workspace
+  const MatDesc* d = g_log.front().d;
+  CHECK(reinterpret_cast<const char*>(d) == ws, "%s: descriptor table at the workspace base", name);
+  CHECK(g_log.front().n == n_active, "%s: %d descriptors, want %d", name, g_log.front().n, n_active);
+  std::vector<std::pair<uintptr_t, uintptr_t>> regions;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ws), hi = lo + ws_bytes;
+  auto inside = [&](const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return a >= lo && a + bytes <= hi;
+  };
+  for (int a = 0; a < n_active; ++a) {
+    const MatDesc& m = d[a];
+    // class order: 256-tiles, 128-tiles, then the fused class
+    const int t = tile_of(m.rows, m.cols);
+    const int cls = t == kTileBig ? 0 : t == kTileSmall ? 1 : 2;
+    const int want_cls = a < n_big ? 0 : a < n_big + n_small ? 1 : 2;
+    CHECK(cls == want_cls, "%s: descriptor %d in class %d, want %d", name, a, cls, want_cls);
+    const int64_t rp = ceil_to(m.rows, t), cp = ceil_to(m.cols, t);
+    const bool tall = m.rows > m.cols;
+    CHECK(m.rows_pad == rp && m.cols_pad == cp, "%s: descriptor %d padding", name, a);
+    CHECK(m.m_pad == (tall ? cp : rp) && m.n_pad == (tall ? rp : cp), "%s: descriptor %d m/n pad", name, a);
+    CHECK(((m.flags & kFlagTall) != 0) == tall, "%s: descriptor %d tall flag", name, a);
+    CHECK(((m.flags & kFlagSplitC) != 0) == (std::min(m.rows, m.cols) <= kSplitMaxM),
+          "%s: descriptor %d split flag", name, a);
+    CHECK((m.flags & kFlagGradBf16) != 0, "%s: descriptor %d dtype", name, a);
+    const size_t xb = static_cast<size_t>(rp) * cp * 2, ab = static_cast<size_t>(m.m_pad) * m.m_pad * 2;
+    for (int k = 0; k < 2; ++k) {
+      CHECK(inside(m.x[k], xb) && reinterpret_cast<uintptr_t>(m.x[k]) % 256 == 0, "%s: X%d of %d", name, k, a);
+      regions.push_back({reinterpret_cast<uintptr_t>(m.x[k]), reinterpret_cast<uintptr_t>(m.x[k]) + xb});
+    }
+    for (const uint16_t* p : {m.a, m.b}) {
+      CHECK(inside(p, ab) && reinterpret_cast<uintptr_t>(p) % 256 == 0, "%s: A/C of %d", name, a);
+      regions.push_back({reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + ab});
+    }
+    if (m.flags & kFlagSplitC) {
+      CHECK(m.blo && inside(m.blo, ab), "%s: C_lo of %d", name, a);
+      regions.push_back({reinterpret_cast<uintptr_t>(m.blo), reinterpret_cast<uintptr_t>(m.blo) + ab});
+    } else {
+      CHECK(m.blo == nullptr, "%s: C_lo of unsplit %d", name, a);
+    }
+    CHECK(inside(m.nrm2, 8), "%s: norm slot of %d", name, a);
+    regions.push_back({reinterpret_cast<uintptr_t>(m.nrm2), reinterpret_cast<uintptr_t>(m.nrm2) + 8});
+    CHECK(inside(m.colsum, static_cast<size_t>(m.cols) * 8), "%s: column sums of %d", name, a);
+    regions.push_back({reinterpret_cast<uintptr_t>(m.colsum),
+                       reinterpret_cast<uintptr_t>(m.colsum) + static_cast<size_t>(m.cols) * 8});
+  }
+  std::sort(regions.begin(), regions.end());
+  for (size_t k = 1; k < regions.size(); ++k)
+    CHECK(regions[k].first >= regions[k - 1].second, "%s: workspace regions overlap", name);
+  // every active matrix's caller pointers appear exactly once
+  std::vector<const float*> params;
+  for (int a = 0; a < n_active; ++a) params.push_back(d[a].param);
+  std::sort(params.begin(), params.end());
+  CHECK(std::adjacent_find(params.begin(), params.end()) == params.end(), "%s: a parameter twice", name);
+  for (int64_t i = 0; i < n; ++i)
+    CHECK(std::binary_search(params.begin(), params.end(), mats[i].param) == (mats[i].grad != nullptr),
+          "%s: matrix %lld presence", name, static_cast<long long>(i));
+
+  // per-launch units against the prefix arrays and the tile counts
+  int step_of_gram2 = 0;
+  for (const Launch& l : g_log) {
+    if (l.phase == "gram" || l.phase == "gram2" || l.phase == "xupdate") {
+      const bool sym = l.phase != "xupdate";
+      CHECK(l.prefix[0] == 0 && l.prefix[l.n] == l.units, "%s: %s units %lld, prefix total %lld", name,
+            l.phase.c_str(), static_cast<long long>(l.units), static_cast<long long>(l.prefix[l.n]));
+      for (int i = 0; i < l.n; ++i) {
+        const MatDesc& m = l.d[i];
+        CHECK(m.m_pad % l.tile == 0 && m.n_pad % l.tile == 0, "%s: %s tile %d", name, l.phase.c_str(), l.tile);
+        const int64_t ts = m.m_pad / l.tile;
+        const int64_t own = sym ? ts * (ts + 1) / 2 : (m.rows_pad / l.tile) * (m.cols_pad / l.tile);
+        CHECK(l.prefix[i + 1] - l.prefix[i] == own, "%s: %s matrix %d owns %lld units, want %lld", name,
+              l.phase.c_str(), i, static_cast<long long>(l.prefix[i + 1] - l.prefix[i]),
+              static_cast<long long>(own));
+      }
+      if (l.phase == "gram2") {
+        const muon_ns_coeff_t& c = cs.coeffs[cs.coeffs.size() == 1 ? 0 : step_of_gram2 / ((n_big > 0) + (n_small > 0))];
+        CHECK(l.a == c.a && l.b == c.b && l.c == c.c, "%s: C launch coefficients", name);
+        ++step_of_gram2;
+      }
+    }
+    if (l.phase == "apply") CHECK(l.parity == (cs.ns & 1), "%s: apply parity %d", name, l.parity);
+  }
+  std::free(raw);
+}
+
+int main(int argc, char** argv) {
+  const std::string which = argc > 1 ? argv[1] : "all";
+  Case mamba;
+  for (int l = 0; l < 24; ++l)
+    for (auto s : {std::make_pair(768, 3072), std::make_pair(1536, 80), std::make_pair(48, 1536),
+                   std::make_pair(1536, 768)})
+      mamba.shapes.push_back(s);
+  Case transformer;  // 8 of the 32 layers (the workspace is host memory here)
+  for (int l = 0; l < 8; ++l) {
+    for (int k = 0; k < 4; ++k) transformer.shapes.push_back({4096, 4096});
+    transformer.shapes.push_back({4096, 14336});
+    transformer.shapes.push_back({4096, 14336});
+    transformer.shapes.push_back({14336, 4096});
+  }
+  Case ragged;
+  unsigned x = 12345u;
+  const int64_t sz[4] = {64, 128, 256, 512};
+  for (int i = 0; i < 2048; ++i) {
+    x = x * 1664525u + 1013904223u;
+    const int64_t r = sz[(x >> 10) & 3];
+    x = x * 1664525u + 1013904223u;
+    ragged.shapes.push_back({r, sz[(x >> 10) & 3]});
+  }
+  Case mixed;  // every class, both orientations, ragged edges, skipped matrices, per-step coefficients
+  mixed.shapes = {{20, 300}, {300, 50}, {96, 200}, {128, 384}, {48, 1536}, {1536, 80}, {130, 700},
+                  {700, 300}, {200, 200}, {1030, 1280}, {1280, 1030}, {1, 1}, {8192, 28672}, {33, 7}};
+  mixed.present = {true, true, false, true, true, true, true, false, true, true, true, true, true, true};
+  mixed.ns = 10;
+  mixed.coeffs.clear();
+  for (int k = 0; k < 10; ++k)
+    mixed.coeffs.push_back(k < 8 ? muon_ns_coeff_t{3.4445f, -4.7750f, 2.0315f} : muon_ns_coeff_t{2.f, -1.5f, 0.5f});
+  if (which == "all" || which == "mamba") run_case("mamba", mamba);
+  if (which == "all" || which == "transformer") run_case("transformer", transformer);
+  if (which == "all" || which == "ragged") run_case("ragged", ragged);
+  if (which == "all" || which == "mixed") run_case("mixed", mixed);
+  if (g_fail) return 1;
+  std::printf("ok\n");
+  return 0;
+}
