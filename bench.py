@@ -253,6 +253,9 @@ def main():
                     help="skip the AdamW-branch measurement (an extra object in the JSON line)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured second denominators (vendor GEMM, device copy)")
+    ap.add_argument("--entry", choices=("eager", "plan", "noalloc"), default="eager",
+                    help="entry point timed: muon_step (default), a prepared plan's step, or "
+                         "muon_step_noalloc (workloads within its fixed scratch only)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -292,6 +295,23 @@ def main():
     stream = torch.cuda.current_stream(dev)
     kw = dict(lr=w.lr, mu=w.mu, wd=w.wd, ns_steps=w.ns_steps, coeffs=QUINTIC,
               rms_scale=w.rms_mode, eps=w.eps, workspace=ws, stream=stream)
+    if args.entry == "eager":
+        def step():
+            muon.muon_step(params, grads, moms, **kw)
+    elif args.entry == "plan":
+        plan = muon.Plan(params, grads, moms, **kw)
+
+        def step():
+            plan.step(stream)
+    else:
+        if muon.workspace_bytes(w.shapes) > muon.NOALLOC_SCRATCH_BYTES:
+            print(f"workload {w.key} needs more workspace than muon_step_noalloc's fixed scratch",
+                  file=sys.stderr)
+            sys.exit(2)
+        nkw = {k: v for k, v in kw.items() if k != "workspace"}
+
+        def step():
+            muon.muon_step_noalloc(params, grads, moms, **nkw)
 
     # device copies of the state the step updates, restored before every step
     p0 = [t.clone() for t in params]
@@ -306,7 +326,7 @@ def main():
 
     for k in range(args.warmup):
         restore()
-        muon.muon_step(params, grads, moms, **kw)
+        step()
         torch.cuda.synchronize()
         log(f"[bench] warmup step {k + 1}/{args.warmup} done")
 
@@ -320,7 +340,7 @@ def main():
     for k in range(args.steps):
         restore()
         ev[k][0].record(stream)
-        muon.muon_step(params, grads, moms, **kw)
+        step()
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -339,7 +359,7 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded device draws of the workload's laws)",
-           "config": {"workload": w.name, "n_matrices": w.n_mats,
+           "config": {"workload": w.name, "n_matrices": w.n_mats, "entry": args.entry,
                       "shapes": sorted({f"{r}x{c}" for r, c in w.shapes}),
                       "grad_dtype": w.grad_dtype, "ns_steps": w.ns_steps,
                       "coeffs": list(QUINTIC), "lr": w.lr, "mu": w.mu, "wd": w.wd,
@@ -353,7 +373,8 @@ def main():
                       "wall_ms_per_step": elapsed * 1e3 / args.steps,
                       "between_steps": "momentum and parameters restored from a device copy"}}
 
-    if phases is not None:
+    if phases is not None and any(r["launches"] for r in phases.values()):
+        # (muon_step_noalloc records no phase timing: no events may be created)
         work = phase_work(w, muon)
         per = {}
         for name, rec in phases.items():
@@ -414,6 +435,8 @@ def main():
         del a, b
         log(f"[bench] copy calibration: {n * 4 / 2**30:.2f} GiB copied")
 
+    if args.entry == "plan":
+        del plan
     del params, grads, moms, ws
     torch.cuda.empty_cache()
     if not args.no_ceilings:
