@@ -697,6 +697,56 @@ int prepare_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
   return MUON_OK;
 }
 
+// The last eager step's workspace plan and descriptor table, per thread.  A
+// training loop steps the same list every iteration; rebuilding both (argument
+// checks, the alias check, the plan, the table) costs about 0.4 ms on the host
+// for 2048 matrices, which a step on small matrices does not hide.  The table
+// is a pure function of the matrix list, the options, the coefficients and
+// the workspace address, all compared byte for byte here, so a hit reuses
+// exactly what a rebuild would produce (it is still uploaded every call: the
+// workspace's contents are not trusted between calls).
+struct StepCache {
+  bool valid = false;
+  std::vector<muon_matrix_t> mats;
+  std::vector<muon_ns_coeff_t> coeffs;
+  int ns_steps = 0, n_coeffs = 0, rms_scale_mode = 0;
+  uint32_t flags = 0, reserved = 0;
+  const void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  Plan plan;
+  Table t;
+
+  bool matches(const muon_matrix_t* m, int64_t n, int ns, const muon_ns_coeff_t* cf, int nc,
+               int rms, const muon_options_t* o, const void* ws, size_t wsb) const {
+    if (!valid || n <= 0 || !m || static_cast<size_t>(n) != mats.size() || ns != ns_steps ||
+        rms != rms_scale_mode || ws != workspace || wsb != workspace_bytes)
+      return false;
+    if ((o ? o->flags : 0u) != flags || (o ? o->reserved : 0u) != reserved) return false;
+    const int ncf = ns > 0 ? nc : 0;
+    if (ncf != static_cast<int>(coeffs.size())) return false;
+    if (ncf > 0 && (!cf || std::memcmp(cf, coeffs.data(), sizeof(muon_ns_coeff_t) * ncf) != 0)) return false;
+    if (ns > 0 && nc != n_coeffs) return false;
+    return std::memcmp(m, mats.data(), sizeof(muon_matrix_t) * mats.size()) == 0;
+  }
+
+  void store(const muon_matrix_t* m, int64_t n, int ns, const muon_ns_coeff_t* cf, int nc, int rms,
+             const muon_options_t* o, const void* ws, size_t wsb) {
+    valid = n > 0 && m != nullptr;
+    if (!valid) return;
+    mats.assign(m, m + n);
+    const int ncf = ns > 0 ? nc : 0;
+    coeffs.assign(cf, cf + ncf);
+    ns_steps = ns;
+    n_coeffs = nc;
+    rms_scale_mode = rms;
+    flags = o ? o->flags : 0u;
+    reserved = o ? o->reserved : 0u;
+    workspace = ws;
+    workspace_bytes = wsb;
+  }
+};
+thread_local StepCache g_step_cache;
+
 }  // namespace
 
 // A step prepared once over fixed buffers (muon_plan_create).
@@ -728,13 +778,25 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
                  float eps, const muon_options_t* options, void* workspace, size_t workspace_bytes,
                  hipStream_t stream) {
   g_debug = debug_env();
-  Plan plan;
-  Table t;
+  StepCache& c = g_step_cache;
+  if (c.matches(mats, n_mats, ns_steps, coeffs, n_coeffs, rms_scale_mode, options, workspace,
+                workspace_bytes)) {
+    // the list, options and workspace of the last successful call: its plan
+    // and table are what a rebuild would produce; only the scalars are new
+    if (!finite(lr) || !finite(mu) || !finite(wd) || !(eps >= 0.0f) || !finite(eps)) return MUON_EINVAL;
+    if (c.t.n_active == 0) return MUON_OK;
+    return run_sequence(c.plan, c.t, static_cast<char*>(workspace), false, lr, mu, wd, ns_steps,
+                        coeffs, n_coeffs, eps, stream);
+  }
+  c.valid = false;
   const int rc = prepare_step(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs,
-                              rms_scale_mode, eps, options, workspace, workspace_bytes, plan, t);
-  if (rc != MUON_OK || t.n_active == 0) return rc;
-  return run_sequence(plan, t, static_cast<char*>(workspace), false, lr, mu, wd, ns_steps, coeffs,
-                      n_coeffs, eps, stream);
+                              rms_scale_mode, eps, options, workspace, workspace_bytes, c.plan, c.t);
+  if (rc != MUON_OK) return rc;
+  c.store(mats, n_mats, ns_steps, coeffs, n_coeffs, rms_scale_mode, options, workspace,
+          workspace_bytes);
+  if (c.t.n_active == 0) return MUON_OK;
+  return run_sequence(c.plan, c.t, static_cast<char*>(workspace), false, lr, mu, wd, ns_steps,
+                      coeffs, n_coeffs, eps, stream);
 }
 
 int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd, int ns_steps,

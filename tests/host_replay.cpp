@@ -144,6 +144,9 @@ struct Case {
   std::vector<muon_ns_coeff_t> coeffs{{3.4445f, -4.7750f, 2.0315f}};
 };
 
+static void check_call(const char* name, const Case& cs, std::vector<muon_matrix_t>& mats, char* ws,
+                       size_t ws_bytes);
+
 static void run_case(const char* name, const Case& cs) {
   const int64_t n = static_cast<int64_t>(cs.shapes.size());
   std::vector<muon_matrix_t> mats(n);
@@ -164,12 +167,28 @@ static void run_case(const char* name, const Case& cs) {
   // the workspace: host memory standing in for device memory (untouched pages stay virtual)
   char* raw = static_cast<char*>(std::malloc(ws_bytes + 256));
   char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(raw) + 255) & ~uintptr_t(255));
+  // the same list twice (the second call reuses the first one's plan and
+  // table), then with the first matrix's gradient toggled (rebuilt)
+  check_call(name, cs, mats, ws, ws_bytes);
+  std::memset(ws, 0xA5, std::min<size_t>(ws_bytes, 1 << 22));   // the table is uploaded anew
+  check_call(name, cs, mats, ws, ws_bytes);
+  Case cs2 = cs;
+  if (cs2.present.empty()) cs2.present.assign(static_cast<size_t>(n), true);
+  cs2.present[0] = !cs2.present[0];
+  mats[0].grad = cs2.present[0] ? reinterpret_cast<void*>(0x100000000000ull + 0x80000000ull) : nullptr;
+  check_call(name, cs2, mats, ws, ws_bytes);
+  std::free(raw);
+}
+
+static void check_call(const char* name, const Case& cs, std::vector<muon_matrix_t>& mats, char* ws,
+                       size_t ws_bytes) {
+  const int64_t n = static_cast<int64_t>(mats.size());
   g_log.clear();
   const int rc = muon_step(mats.data(), n, 0.02f, 0.95f, 0.01f, cs.ns, cs.coeffs.data(),
                            static_cast<int>(cs.coeffs.size()), MUON_SCALE_NONE, 1e-7f, ws, ws_bytes,
                            nullptr);
   CHECK(rc == MUON_OK, "%s: muon_step returned %d", name, rc);
-  if (rc != MUON_OK) { std::free(raw); return; }
+  if (rc != MUON_OK) return;
 
   // expected classes, from the shapes alone (the kernels' class rules)
   auto fused = [](int64_t r, int64_t c) {
@@ -286,7 +305,6 @@ static void run_case(const char* name, const Case& cs) {
     }
     if (l.phase == "apply") CHECK(l.parity == (cs.ns & 1), "%s: apply parity %d", name, l.parity);
   }
-  std::free(raw);
 }
 
 int main(int argc, char** argv) {
