@@ -19,6 +19,7 @@
 //     skipped matrices (no gradient) have no descriptor.
 // Usage: host_replay <case>; prints "ok" and exits 0, or the first failure.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -137,11 +138,15 @@ static int g_fail = 0;
 
 static int64_t ceil_to(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+enum Entry { kEager = 0, kPlan = 1, kOrtho = 2 };
 struct Case {
   std::vector<std::pair<int64_t, int64_t>> shapes;
   std::vector<bool> present;
   int ns = 5;
   std::vector<muon_ns_coeff_t> coeffs{{3.4445f, -4.7750f, 2.0315f}};
+  uint32_t opts = 0;       // MUON_OPT_* of muon_step_ex (eager and plan)
+  int entry = kEager;
+  int rms = MUON_SCALE_NONE;
 };
 
 static void check_call(const char* name, const Case& cs, std::vector<muon_matrix_t>& mats, char* ws,
@@ -167,9 +172,13 @@ static void run_case(const char* name, const Case& cs) {
   // the workspace: host memory standing in for device memory (untouched pages stay virtual)
   char* raw = static_cast<char*>(std::malloc(ws_bytes + 256));
   char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(raw) + 255) & ~uintptr_t(255));
-  // the same list twice (the second call reuses the first one's plan and
-  // table), then with the first matrix's gradient toggled (rebuilt)
+  // the same list twice (the second eager call reuses the first one's plan
+  // and table), then with the first matrix's gradient toggled (rebuilt)
   check_call(name, cs, mats, ws, ws_bytes);
+  if (cs.entry != kEager) {
+    std::free(raw);
+    return;
+  }
   std::memset(ws, 0xA5, std::min<size_t>(ws_bytes, 1 << 22));   // the table is uploaded anew
   check_call(name, cs, mats, ws, ws_bytes);
   Case cs2 = cs;
@@ -182,13 +191,53 @@ static void run_case(const char* name, const Case& cs) {
 
 static void check_call(const char* name, const Case& cs, std::vector<muon_matrix_t>& mats, char* ws,
                        size_t ws_bytes) {
-  const int64_t n = static_cast<int64_t>(mats.size());
+  const int64_t n_all = static_cast<int64_t>(mats.size());
   g_log.clear();
-  const int rc = muon_step(mats.data(), n, 0.02f, 0.95f, 0.01f, cs.ns, cs.coeffs.data(),
-                           static_cast<int>(cs.coeffs.size()), MUON_SCALE_NONE, 1e-7f, ws, ws_bytes,
-                           nullptr);
-  CHECK(rc == MUON_OK, "%s: muon_step returned %d", name, rc);
+  const muon_options_t opt{cs.opts, 0u};
+  int rc = MUON_OK;
+  std::vector<muon_ortho_t> orth;
+  if (cs.entry == kEager) {
+    rc = muon_step_ex(mats.data(), n_all, 0.02f, 0.95f, 0.01f, cs.ns, cs.coeffs.data(),
+                      static_cast<int>(cs.coeffs.size()), cs.rms, 1e-7f, &opt, ws, ws_bytes, nullptr);
+  } else if (cs.entry == kPlan) {
+    muon_plan_t* plan = nullptr;
+    rc = muon_plan_create(mats.data(), n_all, cs.ns, cs.coeffs.data(), static_cast<int>(cs.coeffs.size()),
+                          cs.rms, 1e-7f, &opt, ws, ws_bytes, nullptr, &plan);
+    CHECK(g_log.empty(), "%s: plan creation launched kernels", name);
+    const float hyper[3] = {0.02f, 0.95f, 0.01f};          // "device" floats
+    if (rc == MUON_OK) rc = muon_plan_step(plan, hyper, nullptr);
+    muon_plan_destroy(plan);
+    // a plan step first clears the norm slots with a fill kernel
+    CHECK(!g_log.empty() && g_log.front().phase == "fill", "%s: plan step without its fill", name);
+    if (!g_log.empty()) g_log.erase(g_log.begin());
+  } else {
+    // orthogonalisation alone: in = the gradient, out = a bf16 buffer at the parameter's address;
+    // skipped matrices are left out of the list
+    std::vector<muon_matrix_t> kept;
+    for (const muon_matrix_t& m : mats)
+      if (m.grad) {
+        muon_ortho_t o;
+        o.in = m.grad;
+        o.out = m.param;
+        o.rows = m.rows;
+        o.cols = m.cols;
+        o.in_dtype = m.grad_dtype;
+        orth.push_back(o);
+        kept.push_back(m);
+      }
+    mats = kept;
+    rc = orth.empty() ? MUON_OK
+                      : muon_orthogonalize(orth.data(), static_cast<int64_t>(orth.size()), cs.ns,
+                                           cs.coeffs.data(), static_cast<int>(cs.coeffs.size()), 1e-7f,
+                                           ws, ws_bytes, nullptr);
+  }
+  CHECK(rc == MUON_OK, "%s: entry %d returned %d", name, cs.entry, rc);
   if (rc != MUON_OK) return;
+  const int64_t n = static_cast<int64_t>(mats.size());      // (orthogonalise: the present ones)
+  if (mats.empty() || g_log.empty()) {
+    CHECK(g_log.empty(), "%s: launches for an empty list", name);
+    return;
+  }
 
   // expected classes, from the shapes alone (the kernels' class rules)
   auto fused = [](int64_t r, int64_t c) {
@@ -206,10 +255,30 @@ static void check_call(const char* name, const Case& cs, std::vector<muon_matrix
     (t == kTileBig ? n_big : t == kTileSmall ? n_small : n_fused) += 1;
   }
 
+  if (n_active == 0) {
+    CHECK(g_log.empty(), "%s: launches with every gradient absent", name);
+    return;
+  }
   // the launch sequence
-  std::vector<std::string> want{"momentum", "normalize"};
+  std::vector<std::string> want;
+  if (cs.opts & MUON_OPT_ZERO_CENTER) want.push_back("colsum");
+  want.push_back("momentum");
+  want.push_back("normalize");
   int fused_launches = 0;
   for (const Launch& l : g_log) fused_launches += l.phase == "fused";
+  {
+    // one fused launch per padded short side present (when there is an iteration)
+    bool seen[5] = {false, false, false, false, false};
+    int classes = 0;
+    for (int64_t i = 0; i < n; ++i)
+      if (mats[i].grad && tile_of(mats[i].rows, mats[i].cols) == kTileFused) {
+        const int k = static_cast<int>(ceil_to(std::min(mats[i].rows, mats[i].cols), kTileFused) / kTileFused);
+        if (!seen[k]) classes += 1;
+        seen[k] = true;
+      }
+    CHECK(fused_launches == (cs.ns > 0 ? classes : 0), "%s: %d fused launches, want %d", name,
+          fused_launches, cs.ns > 0 ? classes : 0);
+  }
   for (int f = 0; f < fused_launches; ++f) want.push_back("fused");
   for (int k = 0; k < ((n_big + n_small) ? cs.ns : 0); ++k)
     for (const char* ph : {"gram", "gram2", "xupdate"}) {
@@ -272,13 +341,32 @@ static void check_call(const char* name, const Case& cs, std::vector<muon_matrix
   std::sort(regions.begin(), regions.end());
   for (size_t k = 1; k < regions.size(); ++k)
     CHECK(regions[k].first >= regions[k - 1].second, "%s: workspace regions overlap", name);
-  // every active matrix's caller pointers appear exactly once
-  std::vector<const float*> params;
-  for (int a = 0; a < n_active; ++a) params.push_back(d[a].param);
-  std::sort(params.begin(), params.end());
-  CHECK(std::adjacent_find(params.begin(), params.end()) == params.end(), "%s: a parameter twice", name);
+  // every active matrix's caller pointers appear exactly once (orthogonalisation:
+  // its input and output), and the step variants travel in the flags
+  std::vector<const void*> grads;
+  for (int a = 0; a < n_active; ++a) {
+    grads.push_back(d[a].grad);
+    if (cs.entry == kOrtho) {
+      CHECK(d[a].param == nullptr && d[a].mom == nullptr && d[a].out != nullptr, "%s: ortho descriptor %d", name, a);
+    } else {
+      CHECK(d[a].out == nullptr && d[a].param != nullptr && d[a].mom != nullptr, "%s: step descriptor %d", name, a);
+      const uint32_t want_flags = ((cs.opts & MUON_OPT_ZERO_CENTER) ? kFlagZeroCenter : 0u) |
+                                  ((cs.opts & MUON_OPT_NESTEROV) ? kFlagNesterov : 0u) |
+                                  ((cs.opts & MUON_OPT_NS_FIRST) ? kFlagNsFirst : 0u);
+      CHECK((d[a].flags & (kFlagZeroCenter | kFlagNesterov | kFlagNsFirst)) == want_flags,
+            "%s: variant flags of %d", name, a);
+    }
+    const double want_scale = cs.rms == MUON_SCALE_SQRT_MAX1
+                                  ? std::sqrt(std::max(1.0, double(d[a].rows) / double(d[a].cols)))
+                                  : 1.0;
+    CHECK(cs.entry == kOrtho || std::fabs(d[a].scale - want_scale) <= 1e-6 * want_scale,
+          "%s: scale of %d", name, a);
+  }
+  std::sort(grads.begin(), grads.end());
+  CHECK(std::adjacent_find(grads.begin(), grads.end()) == grads.end(), "%s: a gradient twice", name);
   for (int64_t i = 0; i < n; ++i)
-    CHECK(std::binary_search(params.begin(), params.end(), mats[i].param) == (mats[i].grad != nullptr),
+    CHECK(std::binary_search(grads.begin(), grads.end(), static_cast<const void*>(mats[i].grad)) ==
+              (mats[i].grad != nullptr),
           "%s: matrix %lld presence", name, static_cast<long long>(i));
 
   // per-launch units against the prefix arrays and the tile counts
@@ -338,6 +426,45 @@ int main(int argc, char** argv) {
   mixed.coeffs.clear();
   for (int k = 0; k < 10; ++k)
     mixed.coeffs.push_back(k < 8 ? muon_ns_coeff_t{3.4445f, -4.7750f, 2.0315f} : muon_ns_coeff_t{2.f, -1.5f, 0.5f});
+  if (which == "random") {
+    // a seeded random list: shapes across every kernel class and both
+    // orientations (sides 1..4000, mostly small), a tenth of the gradients
+    // absent, 0..12 Newton-Schulz steps with one or per-step coefficients,
+    // any accepted variant combination, RMS scale on or off, and the eager,
+    // plan or orthogonalise entry
+    const unsigned seed = argc > 2 ? static_cast<unsigned>(std::atoi(argv[2])) : 1u;
+    unsigned r = seed * 2654435761u + 12345u;
+    auto next = [&r](unsigned mod) {
+      r = r * 1664525u + 1013904223u;
+      return (r >> 8) % mod;
+    };
+    auto side = [&]() -> int64_t {
+      const unsigned k = next(100);
+      if (k < 35) return 1 + next(32);
+      if (k < 65) return 33 + next(96);
+      if (k < 93) return 129 + next(900);
+      return 1000 + next(3000);
+    };
+    Case rc;
+    const int n = 1 + static_cast<int>(next(160));
+    for (int i = 0; i < n; ++i) {
+      rc.shapes.push_back({side(), side()});
+      rc.present.push_back(next(10) != 0);
+    }
+    rc.ns = static_cast<int>(next(13));
+    rc.coeffs.clear();
+    const int nc = (next(2) == 0 || rc.ns == 0) ? 1 : rc.ns;
+    for (int k = 0; k < nc; ++k)
+      rc.coeffs.push_back({1.0f + 0.25f * next(10), -0.5f - 0.25f * next(16), 0.1f * next(25)});
+    const uint32_t combos[6] = {0u, MUON_OPT_ZERO_CENTER, MUON_OPT_NESTEROV, MUON_OPT_NS_FIRST,
+                                MUON_OPT_ZERO_CENTER | MUON_OPT_NESTEROV,
+                                MUON_OPT_ZERO_CENTER | MUON_OPT_NS_FIRST};
+    rc.entry = static_cast<int>(next(3));
+    rc.opts = rc.entry == kOrtho ? 0u : combos[next(6)];
+    rc.rms = next(2) ? MUON_SCALE_SQRT_MAX1 : MUON_SCALE_NONE;
+    const std::string nm = "random " + std::to_string(seed);
+    run_case(nm.c_str(), rc);
+  }
   if (which == "all" || which == "mamba") run_case("mamba", mamba);
   if (which == "all" || which == "transformer") run_case("transformer", transformer);
   if (which == "all" || which == "ragged") run_case("ragged", ragged);
