@@ -3,6 +3,7 @@
     python -m matrix_aware_optimizer_libmuon_amd.profiling trace  <kernel_stats.csv> <title> <command>
     python -m matrix_aware_optimizer_libmuon_amd.profiling traffic <fetch.csv> <write.csv> <title> <commands>
     python -m matrix_aware_optimizer_libmuon_amd.profiling mfma <counters.csv> <kernel_trace.csv> <title> <command>
+    python -m matrix_aware_optimizer_libmuon_amd.profiling counters <counters.csv> <title> <command>
 
 The MFMA summary records, per Newton-Schulz GEMM kernel, the fraction of
 cycles the MFMA units were busy (rocprofv3's MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES
@@ -152,6 +153,26 @@ def mfma_summary(counters_csv: str, trace_csv: str, title: str, command: str) ->
     return "\n".join(out) + "\n"
 
 
+def counters_summary(counters_csv: str, title: str, command: str) -> str:
+    """Mean value per dispatch of every counter in the run, for each libmuon
+    kernel (rocprofv3 sums a counter over its hardware instances)."""
+    rows = list(csv.DictReader(open(counters_csv)))
+    names = sorted({r["Counter_Name"] for r in rows})
+    kernels = [k for k in PHASE_OF if any(_short(r["Kernel_Name"]) == k for r in rows)]
+    kernels += sorted({_short(r["Kernel_Name"]) for r in rows if _short(r["Kernel_Name"]).startswith(
+        ("k_gram<128>", "k_gram2<128>", "k_xupdate<128>", "k_ns_fused"))} - set(kernels))
+    vals = {n: _per_kernel_counter(counters_csv, n) for n in names}
+    out = [f"# {title}", "", "Command (repository root, one MI355X; counters in their own run):", "",
+           "```", command, "```", "",
+           "Mean per dispatch. GRBM_GUI_ACTIVE is summed over the 8 XCDs (cycles per XCD = value / 8); "
+           "MfmaUtil is a percentage of MFMA-busy SIMD cycles; SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = bf16 "
+           "flops issued; TCC_* count L2 requests, hits and misses over all channels.", "",
+           "| kernel | " + " | ".join(names) + " |", "|---|" + "---:|" * len(names)]
+    for k in kernels:
+        out.append(f"| `{k}` | " + " | ".join(f"{vals[n].get(k, float('nan')):.4g}" for n in names) + " |")
+    return "\n".join(out) + "\n"
+
+
 def _per_kernel_counter(csv_path: str, counter: str) -> dict:
     acc = defaultdict(list)
     for r in csv.DictReader(open(csv_path)):
@@ -197,6 +218,8 @@ if __name__ == "__main__":
         sys.stdout.write(trace_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif sys.argv[1] == "traffic":
         sys.stdout.write(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
+    elif sys.argv[1] == "counters":
+        sys.stdout.write(counters_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif sys.argv[1] == "mfma":
         sys.stdout.write(mfma_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
     else:
