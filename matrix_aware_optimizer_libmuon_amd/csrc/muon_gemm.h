@@ -99,6 +99,14 @@ __device__ __forceinline__ int opaque_tid() {
 // these writes and wait for all of them.  Ordering is explicit instead:
 // vm_wait<> on the issuing wave, then an LDS barrier, before any wave reads
 // the stage.  The scalar base is wave-uniform by construction.
+// Wait states: on gfx9 a memory instruction that reads a scalar register
+// written by a vector instruction (v_readfirstlane_b32) must come 5 wait
+// states after it.  The compiler pads its own loads for this but not an asm
+// statement, and a load issued early takes the register's previous contents
+// as its address.  So every caller forms `sbase` from scalar values (kernel
+// arguments, block index, descriptor fields, a wave index taken through
+// readfirstlane once, up front), and the readfirstlane below then folds away;
+// tests/test_isa_hazards.py checks the compiled kernels for it.
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint16_t* lds_dst) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) void*)lds_dst));
@@ -412,9 +420,12 @@ __device__ __forceinline__ void store_sym(const f32x4_t (&acc)[Geo<TILE>::NB][Ge
     constexpr int CPB = 64 / UPC;             // columns per 1 KB wave load
     constexpr int BPW = TILE / CPB / 4;       // wave loads per wave
     const uint32_t lb = static_cast<uint32_t>(ld * 2);
+    // the wave index as a scalar, so that the load bases below are formed
+    // by scalar instructions (see dma16)
+    const int ws = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll 8
     for (int q = 0; q < BPW; ++q) {
-      const int blk = w * BPW + q, col = blk * CPB + lane / UPC, u = lane % UPC;
+      const int blk = ws * BPW + q, col = blk * CPB + lane / UPC, u = lane % UPC;
       dma16(reinterpret_cast<const char*>(src + (c0 + blk * CPB) * ld + r0),
             (lane / UPC) * lb + 16u * static_cast<uint32_t>(u ^ (col & 15)), smem + blk * 512);
     }

@@ -1,6 +1,9 @@
 """The tail split of the symmetric launches against the fp64 oracle (a design
-that was tried and is not in the library: its first GPU run faulted and the
-cause is not shown, so these tests stay skipped; see the design notes).
+that was tried and is not in the library: its first GPU run faulted.  Its
+compiled kernels formed load bases with v_readfirstlane_b32 0 wait states
+before the asm loads that read them (tests/test_isa_hazards.py holds the
+library to 5), so a load could take a stale base.  These tests stay skipped
+while the split is out of the library).
 
 26 matrices of the 256-tile class (13 tall 2048 x 1024, 13 wide 1024 x 2048)
 have 260 upper tiles: one full wave of 256 and a tail of 4, so the last 4
@@ -25,8 +28,9 @@ from oracle import muon_oracle as O
 from tests.gpu_helpers import DEV, Run, check_apply_consistency, grad_tensor, rel, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skip(
-    reason="the tail split faulted the GPU (illegal address) on its first run here and its "
-           "cause is not shown; the split is not in the library until it is")]
+    reason="the tail split faulted the GPU (illegal address) on its first run: its load bases "
+           "were written by vector instructions 0 wait states before the loads; the split is "
+           "not in the library")]
 
 SHAPES = [(2048, 1024)] * 13 + [(1024, 2048)] * 13
 
