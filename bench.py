@@ -21,7 +21,10 @@ reported too.  Prints ONE JSON line:
 * measured_ceiling: second denominators measured on this GPU (the
   platform's bf16 GEMM on the X-update products, a device copy);
 * cpu_baseline: the fp64 oracle timed on a bounded sample of the same
-  workload on this host.
+  workload on this host;
+* telemetry: board power and GFX clock sampled (read-only, amdsmi) on a side
+  thread over the timed steps, the bf16 MFMA peak at that clock, and the
+  dominant kernel's rate against it (--no-telemetry leaves it out).
 """
 from __future__ import annotations
 
@@ -29,6 +32,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -42,6 +46,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 QUINTIC = (3.4445, -4.7750, 2.0315)
 FUSED_TILE = 32                 # padding granule the library reports for the fused class
 NS_PHASES = ("gram", "gram2_epilogue", "x_update", "ns_fused")
+NOMINAL_CLOCK_MHZ = 2400.0      # the clock the MFMA peak is quoted at
 
 
 def log(*a):
@@ -240,6 +245,115 @@ def bench_adamw(torch, muon, dev, reps: int = 10):
             "algorithmic_per_launch": nbytes}
 
 
+def _num(v):
+    return float(v) if isinstance(v, (int, float)) and not isinstance(v, bool) else None
+
+
+def summarize_telemetry(samples, cap_w, period_s, min_busy=20):
+    """Power and clock over the timed steps.  `samples`: dicts with power_w,
+    gfxclk_mhz, xcd_gfxclk_mhz (one per XCD), hotspot_c and gfx_activity (%);
+    entries the board does not report are None and are left out.  Only
+    samples with the graphics engine at least half busy count (the board
+    refreshes its metrics with a lag, so the first samples of a short run
+    still show it idle); with fewer than `min_busy` of them the statistics
+    are left out."""
+    busy = [x for x in samples if (_num(x.get("gfx_activity")) or 0.0) >= 50.0]
+    out = {"source": "amdsmi gpu metrics, read-only", "samples": len(samples),
+           "busy_samples": len(busy), "period_ms": period_s * 1e3, "power_cap_w": cap_w}
+    if len(busy) < min_busy:
+        out["note"] = "too few samples with the GPU busy (timed region too short)"
+        return out
+    samples = busy
+    pw = np.array([v for v in (_num(x.get("power_w")) for x in samples) if v is not None])
+    ck = np.array([v for v in (_num(x.get("gfxclk_mhz")) for x in samples) if v is not None])
+    if pw.size:
+        out["power_w"] = {"median": float(np.median(pw)), "p10": float(np.percentile(pw, 10)),
+                          "p90": float(np.percentile(pw, 90)), "max": float(pw.max())}
+        if cap_w:
+            out["power_median_frac_of_cap"] = float(np.median(pw)) / cap_w
+    if ck.size:
+        med = float(np.median(ck))
+        out["gfxclk_mhz"] = {"median": med, "p10": float(np.percentile(ck, 10)),
+                             "p90": float(np.percentile(ck, 90))}
+        out["bf16_peak_at_median_clock_tflops"] = BF16_PEAK_TFLOPS * med / NOMINAL_CLOCK_MHZ
+    xcd = [x.get("xcd_gfxclk_mhz") for x in samples]
+    xcd = [r for r in xcd if isinstance(r, list) and r and all(_num(v) is not None for v in r)]
+    if xcd and len({len(r) for r in xcd}) == 1:
+        out["xcd_gfxclk_mhz_median"] = [float(v) for v in np.median(np.array(xcd, float), axis=0)]
+    hot = [v for v in (_num(x.get("hotspot_c")) for x in samples) if v is not None]
+    if hot:
+        out["hotspot_c_max"] = max(hot)
+    return out
+
+
+class Telemetry:
+    """Board power and GFX clock read from amdsmi on a side thread while the
+    timed steps run.  Read-only queries; without the tooling (or a board that
+    refuses them) the JSON line carries the error instead.  Standard output is
+    pointed at standard error meanwhile, so that nothing the tooling prints can
+    land beside the JSON line."""
+    PERIOD_S = 0.05
+
+    def __init__(self):
+        self.samples, self.error, self.cap_w = [], None, None
+        self._stop = threading.Event()
+        self._th = None
+        self._smi = None
+        self._saved_stdout = None
+
+    def start(self):
+        sys.stdout.flush()
+        self._saved_stdout = os.dup(1)
+        os.dup2(2, 1)
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = _num(amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap"))
+            self.cap_w = cap / 1e6 if cap else None          # reported in microwatts
+        except Exception as e:                                 # no tooling: no telemetry
+            self.error = repr(e)
+            return
+        self._th = threading.Thread(target=self._run, daemon=True)
+        self._th.start()
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+            except Exception as e:
+                self.error = repr(e)
+                return
+            self.samples.append({"power_w": m.get("current_socket_power"),
+                                 "gfxclk_mhz": m.get("current_gfxclk"),
+                                 "xcd_gfxclk_mhz": m.get("current_gfxclks"),
+                                 "hotspot_c": m.get("temperature_hotspot"),
+                                 "gfx_activity": m.get("average_gfx_activity")})
+            self._stop.wait(self.PERIOD_S)
+
+    def stop(self):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        sys.stdout.flush()
+        if self._saved_stdout is not None:
+            os.dup2(self._saved_stdout, 1)
+            os.close(self._saved_stdout)
+            self._saved_stdout = None
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        out = summarize_telemetry(self.samples, self.cap_w, self.PERIOD_S)
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +370,8 @@ def main():
     ap.add_argument("--entry", choices=("eager", "plan", "noalloc"), default="eager",
                     help="entry point timed: muon_step (default), a prepared plan's step, or "
                          "muon_step_noalloc (workloads within its fixed scratch only)")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="do not sample board power and clock over the timed steps")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -336,6 +452,9 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
+    tele = None if args.no_telemetry else Telemetry()
+    if tele is not None:
+        tele.start()
     t_start = time.perf_counter()
     for k in range(args.steps):
         restore()
@@ -344,6 +463,7 @@ def main():
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    telemetry = tele.stop() if tele is not None else None
     phases = muon.timing_read() if not args.no_phase_timing else None
     muon.timing_enable(False)
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
@@ -424,6 +544,11 @@ def main():
                            "traffic": d["traffic"]}
         if "mfma_busy_per_cycle" in d:
             out["roofline"]["mfma_busy_per_cycle"] = d["mfma_busy_per_cycle"]
+        if telemetry and d["bound"] == "mfma" and "bf16_peak_at_median_clock_tflops" in telemetry:
+            telemetry["roofline_kernel_frac_of_clock_peak"] = (
+                d["achieved"] / telemetry["bf16_peak_at_median_clock_tflops"])
+    if telemetry is not None:
+        out["telemetry"] = telemetry
 
     if args.copy_gib > 0:
         n = int(args.copy_gib * 2**30) // 4

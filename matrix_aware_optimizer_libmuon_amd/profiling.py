@@ -4,6 +4,7 @@
     python -m matrix_aware_optimizer_libmuon_amd.profiling traffic <fetch.csv> <write.csv> <title> <commands>
     python -m matrix_aware_optimizer_libmuon_amd.profiling mfma <counters.csv> <kernel_trace.csv> <title> <command>
     python -m matrix_aware_optimizer_libmuon_amd.profiling counters <counters.csv> <title> <command>
+    python -m matrix_aware_optimizer_libmuon_amd.profiling telemetry <bench.json> <title> <command>
 
 The MFMA summary records, per Newton-Schulz GEMM kernel, the fraction of
 cycles the MFMA units were busy (rocprofv3's MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES
@@ -153,6 +154,47 @@ def mfma_summary(counters_csv: str, trace_csv: str, title: str, command: str) ->
     return "\n".join(out) + "\n"
 
 
+def telemetry_summary(bench_json: str, title: str, command: str) -> str:
+    """Board power and GFX clock over bench.py's timed steps (its `telemetry`
+    object), with the step time and the dominant kernel's rate beside them."""
+    with open(bench_json) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    t, r = d.get("telemetry") or {}, d.get("roofline") or {}
+    out = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
+           "Sampled every {:.0f} ms from the board's metrics (read-only) over the timed steps; only "
+           "samples with the graphics engine at least half busy count ({} of {}).".format(
+               t.get("period_ms", float("nan")), t.get("busy_samples"), t.get("samples")), "",
+           "| quantity | value |", "|---|---|",
+           f"| step time (median) | {d.get('ms_per_step', float('nan')):.1f} ms |"]
+    if "power_w" in t:
+        p = t["power_w"]
+        out.append(f"| board power: median / p10 / p90 / max | {p['median']:.0f} / {p['p10']:.0f} / "
+                   f"{p['p90']:.0f} / {p['max']:.0f} W |")
+    if t.get("power_cap_w"):
+        out.append(f"| power cap | {t['power_cap_w']:.0f} W |")
+    if "power_median_frac_of_cap" in t:
+        out.append(f"| median power / cap | {t['power_median_frac_of_cap']:.3f} |")
+    if "gfxclk_mhz" in t:
+        c = t["gfxclk_mhz"]
+        out.append(f"| GFX clock: median / p10 / p90 | {c['median']:.0f} / {c['p10']:.0f} / "
+                   f"{c['p90']:.0f} MHz (2400 MHz nominal) |")
+    if "xcd_gfxclk_mhz_median" in t:
+        out.append("| per-XCD clock medians | " + ", ".join(f"{v:.0f}" for v in t["xcd_gfxclk_mhz_median"])
+                   + " MHz |")
+    if "hotspot_c_max" in t:
+        out.append(f"| hotspot temperature, max | {t['hotspot_c_max']:.0f} C |")
+    if "bf16_peak_at_median_clock_tflops" in t:
+        out.append(f"| bf16 MFMA peak at the median clock | {t['bf16_peak_at_median_clock_tflops']:.0f} "
+                   f"TFLOP/s |")
+    if r:
+        out.append(f"| dominant kernel (`{r.get('kernel')}`) | {r.get('achieved', float('nan')):.0f} "
+                   f"{r.get('unit', '')}: {r.get('frac', float('nan')):.3f} of the quoted peak, "
+                   f"{t.get('roofline_kernel_frac_of_clock_peak', float('nan')):.3f} of the peak at "
+                   f"the median clock |")
+    out += ["", "```json", json.dumps(t), "```"]
+    return "\n".join(out) + "\n"
+
+
 def counters_summary(counters_csv: str, title: str, command: str) -> str:
     """Mean value per dispatch of every counter in the run, for each libmuon
     kernel (rocprofv3 sums a counter over its hardware instances)."""
@@ -220,6 +262,8 @@ if __name__ == "__main__":
         sys.stdout.write(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
     elif sys.argv[1] == "counters":
         sys.stdout.write(counters_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif sys.argv[1] == "telemetry":
+        sys.stdout.write(telemetry_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif sys.argv[1] == "mfma":
         sys.stdout.write(mfma_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
     else:

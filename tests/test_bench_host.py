@@ -78,3 +78,44 @@ def test_issued_work_of_the_symmetric_kernels():
     assert issued["gram"] / work["gram"][1] == pytest.approx(136 / 256)
     assert issued["gram2_epilogue"] / work["gram2_epilogue"][1] == pytest.approx(136 / 256)
     assert issued["x_update"] == work["x_update"][1]
+
+
+def test_telemetry_summary():
+    """Medians and percentiles over the samples; entries the board reports as
+    'N/A' (or not at all) are left out; the peak at the median clock scales
+    the quoted bf16 peak by median clock / 2400 MHz."""
+    samples = [{"power_w": p, "gfxclk_mhz": c, "xcd_gfxclk_mhz": [c - 10, c + 10], "hotspot_c": t,
+                "gfx_activity": 100}
+               for p, c, t in [(1300, 1700, 50), (1350, 1750, 55), (1400, 1800, 58)]]
+    samples.append({"power_w": "N/A", "gfxclk_mhz": None, "xcd_gfxclk_mhz": "N/A", "hotspot_c": "N/A",
+                    "gfx_activity": 100})
+    # an idle reading (the board's metrics lag the start of the run) is left out
+    samples.append({"power_w": 260, "gfxclk_mhz": 177, "xcd_gfxclk_mhz": [177, 177], "hotspot_c": 45,
+                    "gfx_activity": 0})
+    t = bench.summarize_telemetry(samples, 1400.0, 0.05, min_busy=3)
+    assert t["samples"] == 5 and t["busy_samples"] == 4 and t["period_ms"] == 50.0
+    assert t["power_w"]["median"] == 1350 and t["power_w"]["max"] == 1400
+    assert t["power_median_frac_of_cap"] == pytest.approx(1350 / 1400)
+    assert t["gfxclk_mhz"]["median"] == 1750
+    assert t["bf16_peak_at_median_clock_tflops"] == pytest.approx(2500.0 * 1750 / 2400)
+    assert t["xcd_gfxclk_mhz_median"] == [1740.0, 1760.0]
+    assert t["hotspot_c_max"] == 58
+    # nothing numeric: only the bookkeeping keys
+    t = bench.summarize_telemetry([{"power_w": "N/A", "gfx_activity": 100}], None, 0.05, min_busy=1)
+    assert "power_w" not in t and "gfxclk_mhz" not in t and t["power_cap_w"] is None
+    # too few busy samples (a short timed region): no figures, a note instead
+    t = bench.summarize_telemetry(samples, 1400.0, 0.05)
+    assert "note" in t and "power_w" not in t and "bf16_peak_at_median_clock_tflops" not in t
+
+
+def test_telemetry_without_a_gpu_reports_an_error_and_restores_stdout(capfd):
+    """Here (no GPU) the tooling cannot sample: stop() returns an error entry
+    and standard output is back on its own file afterwards."""
+    tele = bench.Telemetry()
+    tele.start()
+    os.write(1, b"while sampling\n")   # what a library would write to file 1: on stderr
+    t = tele.stop()
+    os.write(1, b"after\n")
+    out, err = capfd.readouterr()
+    assert "error" in t
+    assert "after" in out and "while sampling" not in out and "while sampling" in err

@@ -70,3 +70,21 @@ def test_kernel_names_are_shortened_past_anonymous_namespaces():
                   "float const*, int, int)") == "k_ns_fused<64>"
     assert _short("void muon::k_gram<256>(muon::MatDesc const*, long const*, int, long, int)") \
         == "k_gram<256>"
+
+
+def test_telemetry_summary_reads_the_last_json_line(tmp_path):
+    tele = {"samples": 10, "busy_samples": 9, "period_ms": 50.0, "power_cap_w": 1400.0,
+            "power_w": {"median": 1360.0, "p10": 1300.0, "p90": 1370.0, "max": 1380.0},
+            "power_median_frac_of_cap": 1360.0 / 1400.0,
+            "gfxclk_mhz": {"median": 1800.0, "p10": 1750.0, "p90": 1900.0},
+            "bf16_peak_at_median_clock_tflops": 1875.0, "roofline_kernel_frac_of_clock_peak": 0.66}
+    line = {"ms_per_step": 505.0, "telemetry": tele,
+            "roofline": {"kernel": "x_update", "achieved": 1237.5, "unit": "TFLOP/s", "frac": 0.495}}
+    p = tmp_path / "bench.json"
+    p.write_text("noise\n" + json.dumps(line) + "\n")
+    text = profiling.telemetry_summary(str(p), "T", "python3 bench.py")
+    assert text.startswith("# T\n") and "python3 bench.py" in text
+    assert "| 1360 / 1300 / 1370 / 1380 W |" in text and "| 1400 W |" in text
+    assert "1800 / 1750 / 1900 MHz" in text and "(9 of 10)" in text
+    assert "0.495 of the quoted peak, 0.660 of the peak at the median clock" in text
+    assert json.loads(text.split("```json\n")[1].split("\n```")[0]) == tele
