@@ -99,9 +99,12 @@ def test_compiler_pads_its_own_load_by_five_wait_states(tmp_path):
 
 
 @needs_hipcc
-def test_gemm_kernels_keep_the_wait_states(tmp_path):
-    units = [(s, extra) for s, extra in build.SOURCES if s.startswith("muon_gemm")]
-    assert units
+def test_device_code_keeps_the_wait_states(tmp_path):
+    """Every device compilation unit of the library, built as build.py builds
+    it: the GEMM units issue the direct loads, the others must pass too (so a
+    direct load added anywhere is checked)."""
+    units = [(s, extra) for s, extra in build.SOURCES if s.endswith(".hip")]
+    assert any(s.startswith("muon_gemm") for s, _ in units)
     jobs = []
     for src, extra in units:
         out = str(tmp_path / (src + ".s"))
@@ -111,7 +114,7 @@ def test_gemm_kernels_keep_the_wait_states(tmp_path):
         assert p.returncode == 0, f"{src}: {log[-2000:]}"
         text = open(out).read()
         n = H.count_loads(text)
-        assert n > 0, src
+        assert n > 0 or not src.startswith("muon_gemm"), src
         bad = H.scan(text)
         assert not bad, f"{src}: {len(bad)} of {n} loads too close to a vector write: " + \
             "; ".join(f"{h.function[:48]} {h.writer} ({h.wait_states})" for h in bad[:5])
