@@ -1,6 +1,7 @@
 """GPU edge cases: the longest side the ABI accepts, many tiny matrices in one
 call, the largest step count with per-step coefficients over every kernel
-class, and calls where almost every gradient is absent."""
+class, calls where almost every gradient is absent, and a non-finite gradient
+in one matrix of a grouped call."""
 import numpy as np
 import pytest
 
@@ -108,3 +109,48 @@ def test_only_one_gradient_present():
             assert rel(run.o(i), out["o"]) <= TOL_NS
         else:
             assert np.array_equal(run.param(i), mi.param) and np.array_equal(run.mom(i), mi.mom)
+
+
+# two matrices per kernel class, wide then tall: fused (short side <= 128 and
+# fits LDS), 128-tile, 256-tile
+_CLASS_SHAPES = {"fused": [(64, 96), (96, 64)], "128": [(256, 768), (768, 256)],
+                 "256": [(1024, 1536), (1536, 1024)]}
+_BF16_BITS = {"nan": 0x7FC0, "inf": 0x7F80}
+
+
+@pytest.mark.parametrize("bad", ["nan", "inf"])
+@pytest.mark.parametrize("cls", ["fused", "128", "256"])
+def test_nonfinite_gradient_stays_in_its_matrix(cls, bad):
+    """One NaN (or +inf) gradient entry in one matrix of a grouped step.  The
+    pages say nothing of it; the plain reading is that the arithmetic carries
+    it: that matrix's momentum is non-finite at that entry only, its norm is
+    non-finite, and NS spreads NaN over its whole O and update, as in the fp64
+    oracle.  Every other matrix of the same launches, in its class and in the
+    others, matches the oracle: the grouped launches keep the matrices' tiles,
+    norm slots and buffers apart."""
+    lr, mu, wd = 0.02, 0.95, 0.01
+    shapes = [s for k in ("fused", "128", "256") for s in _CLASS_SHAPES[k]]
+    inputs = [W.adhoc_inputs(r, c, "bf16", seed=70 + i) for i, (r, c) in enumerate(shapes)]
+    b = shapes.index(_CLASS_SHAPES[cls][0])
+    mi = inputs[b]
+    r0, c0 = mi.rows // 2, mi.cols // 3
+    mi.grad_bits[r0, c0] = _BF16_BITS[bad]
+    mi.grad[r0, c0] = np.float32(np.nan if bad == "nan" else np.inf)
+    run = Run(inputs).step(lr=lr, mu=mu, wd=wd)
+    for i, m in enumerate(inputs):
+        out = O.muon_step_matrix(m.param, m.grad, m.mom, lr=lr, mu=mu, wd=wd)
+        if i == b:
+            mom = run.mom(i)
+            np.testing.assert_array_equal(np.isfinite(mom), np.isfinite(out["m"]))
+            fin = np.isfinite(out["m"])
+            assert fin.sum() == mom.size - 1
+            assert rel(mom[fin], out["m"][fin]) <= TOL_F32
+            assert not np.isfinite(run.nu(i))
+            assert np.isnan(out["o"]).all() and np.isnan(run.o(i)).all()
+            assert np.isnan(run.param(i)).all()
+            say(f"  {cls}/{bad}: matrix {i} {shapes[i]} non-finite as the oracle")
+        else:
+            assert np.isfinite(run.o(i)).all() and np.isfinite(run.param(i)).all()
+            assert rel(run.mom(i), out["m"]) <= TOL_F32
+            assert rel(run.o(i), out["o"]) <= TOL_NS
+            check_apply_consistency(run, i, lr, wd, 1.0)
