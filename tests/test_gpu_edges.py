@@ -1,7 +1,8 @@
 """GPU edge cases: the longest side the ABI accepts, many tiny matrices in one
 call, the largest step count with per-step coefficients over every kernel
-class, calls where almost every gradient is absent, and a non-finite gradient
-in one matrix of a grouped call."""
+class, calls where almost every gradient is absent, a non-finite gradient in
+one matrix of a grouped call, and the transpose equivariance of the wide and
+tall paths."""
 import numpy as np
 import pytest
 
@@ -154,3 +155,30 @@ def test_nonfinite_gradient_stays_in_its_matrix(cls, bad):
             assert rel(run.mom(i), out["m"]) <= TOL_F32
             assert rel(run.o(i), out["o"]) <= TOL_NS
             check_apply_consistency(run, i, lr, wd, 1.0)
+
+
+@pytest.mark.parametrize("cls", ["fused", "128", "256"])
+def test_transpose_equivariance(cls):
+    """NS(G^T) = NS(G)^T ([wmrh] 2.2: the iteration acts on singular values;
+    the transpose rule of [airosetta] newtonschulz5 runs it on the short side
+    either way).  G and G^T in one grouped call take different operand paths:
+    the wide matrix is read K-contiguous, the tall one through the transposing
+    LDS reads, and its X update is the swapped product X^T C.  Both paths
+    round at the same points and sum the same terms in the same K order (one
+    MFMA per 32-deep slice, operands exchanged on the tall path), and the
+    norm's scale is one fp32 value per matrix, so the outputs are the exact
+    transposes of each other (measured so for every class; any difference
+    would mean the two paths compute different sums)."""
+    lr, mu, wd = 0.02, 0.95, 0.01
+    r, c = _CLASS_SHAPES[cls][0]
+    g = W.adhoc_inputs(r, c, "bf16", seed=90, mom_std=0.5)
+    gt = W.MatrixInputs(c, r, np.ascontiguousarray(g.grad.T), np.ascontiguousarray(g.grad_bits.T),
+                        np.ascontiguousarray(g.param.T), np.ascontiguousarray(g.mom.T))
+    run = Run([g, gt]).step(lr=lr, mu=mu, wd=wd)
+    assert np.array_equal(run.mom(1), run.mom(0).T)
+    o, ot = run.o(0), run.o(1)
+    same = np.array_equal(ot, o.T)
+    err = rel(ot, o.T)
+    say(f"  {cls} {r}x{c}: O(G^T) vs O(G)^T rel {err:.3e}, bit-identical {same}")
+    assert same, f"O(G^T) differs from O(G)^T: rel {err:.3e}"
+    assert np.array_equal(run.param(1), run.param(0).T)
