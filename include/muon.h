@@ -45,7 +45,7 @@
  * is modified then.  Kernel faults are asynchronous and surface at the
  * caller's next synchronisation.  muon_status_string() describes a status;
  * after MUON_EHIP it includes the HIP error text of the calling thread's last
- * failure.
+ * failure, after MUON_ENONFINITE the matrix that failed the check.
  *
  * Device: a call works on the calling thread's current HIP device.  Its
  * stream must belong to that device (else MUON_EINVAL, before anything is
@@ -62,6 +62,20 @@
  * kernel that read a value no kernel of the step wrote would leave NaN in the
  * result.  The variable is read at every call.  Not for production: it
  * serialises the host with the device.
+ *
+ * Non-finite check: with MUON_CHECK_FINITE set in the environment (any value
+ * but "0"), muon_step, muon_step_ex and an eager muon_plan_step wait for the
+ * stream at the end of the step and read back the squared Frobenius norms of
+ * the new momenta that the momentum pass already computed (one double per
+ * matrix, in the workspace; the gradient's own under MUON_OPT_NS_FIRST).
+ * When one is NaN or infinite (a NaN or infinite gradient or momentum entry,
+ * or a sum of squares beyond the fp32 range) the call returns MUON_ENONFINITE
+ * and muon_status_string() names the first such matrix (its index in the
+ * call's list).  Detection only: the step has run, and that matrix's
+ * parameter and momentum hold the non-finite values the arithmetic gave
+ * ("Muon meets Mamba", section 6.1, lists NaN among the troubles to watch
+ * for).  Ignored by muon_step_noalloc, and by a muon_plan_step on a
+ * capturing stream (neither may wait or read back).
  *
  * Graph capture: every call stages its descriptor table through a small ring
  * of pinned host buffers that later calls reuse, so a captured copy would
@@ -87,6 +101,7 @@ extern "C" {
 #define MUON_EHIP       -3   /* a HIP runtime call or kernel launch failed    */
 #define MUON_EALIAS     -4   /* param / grad / momentum ranges overlap        */
 #define MUON_ECAPTURE   -5   /* the stream is capturing a graph (see below)    */
+#define MUON_ENONFINITE -6   /* MUON_CHECK_FINITE: a momentum norm is NaN/inf  */
 
 /* ---- element types ----------------------------------------------------- */
 #define MUON_F32  0

@@ -15,7 +15,7 @@ from typing import Iterable, Sequence
 
 from . import _lib
 from ._lib import (MUON_BF16, MUON_EALIAS, MUON_ECAPTURE, MUON_EHIP, MUON_EINVAL,  # noqa: F401
-                   MUON_EWORKSPACE,
+                   MUON_ENONFINITE, MUON_EWORKSPACE,
                    MUON_F32, MUON_OK, MUON_OPT_NESTEROV, MUON_OPT_NS_FIRST, MUON_OPT_ZERO_CENTER,
                    MuonOptions, MUON_SCALE_NONE, MUON_SCALE_SQRT_MAX1, PHASE_NAMES,
                    LibMuonError, MuonAdamWTensor, MuonCoeff, MuonMatrix, MuonOrtho,

@@ -20,6 +20,7 @@ MUON_EWORKSPACE = -2
 MUON_EHIP = -3
 MUON_EALIAS = -4
 MUON_ECAPTURE = -5
+MUON_ENONFINITE = -6
 
 MUON_F32 = 0
 MUON_BF16 = 1

@@ -183,6 +183,19 @@ bool debug_env() {
   return v && v[0] && !(v[0] == '0' && v[1] == 0);
 }
 constexpr uint32_t kBf16NanPair = 0x7FC07FC0u;
+
+// MUON_CHECK_FINITE (environment, read at every call; any value but "" or
+// "0"): at the end of an eager step, wait for the stream and read back the
+// squared momentum norms the momentum pass wrote (one double per matrix, slot
+// i for the caller's matrix i, zero for a skipped one).  A non-finite norm
+// means a NaN or infinite entry in that matrix's new momentum (so in its
+// gradient or old momentum), or a sum of squares beyond the fp32 range.
+thread_local bool g_check_finite = false;
+bool check_finite_env() {
+  const char* v = std::getenv("MUON_CHECK_FINITE");
+  return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
 const char* const kPhaseName[kNumPhases] = {"momentum+norm", "normalise+cast", "Gram X X^T",
                                             "C = aI + bA + cA^2", "X update", "apply",
                                             "AdamW", "fused iteration"};
@@ -211,6 +224,24 @@ hipEvent_t pool_event() {
 int hip_fail(hipError_t e, const std::string& what) {
   g_hip_detail = what + ": " + hipGetErrorString(e);
   return MUON_EHIP;
+}
+
+// MUON_CHECK_FINITE at the end of a step (see g_check_finite).
+int check_norms(const Plan& plan, const char* ws, hipStream_t stream) {
+  if (!g_check_finite || plan.n <= 0) return MUON_OK;
+  std::vector<double> nrm2(static_cast<size_t>(plan.n));
+  hipError_t e = hipMemcpyAsync(nrm2.data(), ws + plan.nrm2_off, nrm2.size() * sizeof(double),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "MUON_CHECK_FINITE read-back of the momentum norms");
+  for (size_t i = 0; i < nrm2.size(); ++i) {
+    if (!std::isfinite(nrm2[i])) {
+      g_hip_detail = "matrix " + std::to_string(i) + ": squared momentum norm is " +
+                     (std::isnan(nrm2[i]) ? "NaN" : "infinite");
+      return MUON_ENONFINITE;
+    }
+  }
+  return MUON_OK;
 }
 
 // False when `stream` belongs to another device than `dev` (a launch there
@@ -778,6 +809,7 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
                  float eps, const muon_options_t* options, void* workspace, size_t workspace_bytes,
                  hipStream_t stream) {
   g_debug = debug_env();
+  g_check_finite = check_finite_env();
   StepCache& c = g_step_cache;
   if (c.matches(mats, n_mats, ns_steps, coeffs, n_coeffs, rms_scale_mode, options, workspace,
                 workspace_bytes)) {
@@ -785,8 +817,9 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
     // and table are what a rebuild would produce; only the scalars are new
     if (!finite(lr) || !finite(mu) || !finite(wd) || !(eps >= 0.0f) || !finite(eps)) return MUON_EINVAL;
     if (c.t.n_active == 0) return MUON_OK;
-    return run_sequence(c.plan, c.t, static_cast<char*>(workspace), false, lr, mu, wd, ns_steps,
-                        coeffs, n_coeffs, eps, stream);
+    const int rc = run_sequence(c.plan, c.t, static_cast<char*>(workspace), false, lr, mu, wd,
+                                ns_steps, coeffs, n_coeffs, eps, stream);
+    return rc != MUON_OK ? rc : check_norms(c.plan, static_cast<const char*>(workspace), stream);
   }
   c.valid = false;
   const int rc = prepare_step(mats, n_mats, lr, mu, wd, ns_steps, coeffs, n_coeffs,
@@ -795,8 +828,9 @@ int muon_step_ex(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, 
   c.store(mats, n_mats, ns_steps, coeffs, n_coeffs, rms_scale_mode, options, workspace,
           workspace_bytes);
   if (c.t.n_active == 0) return MUON_OK;
-  return run_sequence(c.plan, c.t, static_cast<char*>(workspace), false, lr, mu, wd, ns_steps,
-                      coeffs, n_coeffs, eps, stream);
+  const int rc2 = run_sequence(c.plan, c.t, static_cast<char*>(workspace), false, lr, mu, wd,
+                               ns_steps, coeffs, n_coeffs, eps, stream);
+  return rc2 != MUON_OK ? rc2 : check_norms(c.plan, static_cast<const char*>(workspace), stream);
 }
 
 int muon_step(const muon_matrix_t* mats, int64_t n_mats, float lr, float mu, float wd, int ns_steps,
@@ -899,6 +933,9 @@ int muon_plan_step(const muon_plan_t* plan, const float* hyper, hipStream_t stre
                     plan->coeffs.empty() ? nullptr : plan->coeffs.data(), plan->n_coeffs, plan->eps,
                     stream, plan->side.stream ? &plan->side : nullptr);
   g_no_timing = false;
+  // (a capturing stream can neither be waited for nor read back)
+  g_check_finite = check_finite_env();
+  if (rc == MUON_OK && cap == hipStreamCaptureStatusNone) rc = check_norms(plan->plan, ws, stream);
   return rc;
 }
 
@@ -1103,6 +1140,9 @@ const char* muon_status_string(int status) {
              "reused host buffers and cannot be captured";
     case MUON_EHIP:
       s = "HIP error: " + g_hip_detail;
+      return s.c_str();
+    case MUON_ENONFINITE:
+      s = "non-finite values (MUON_CHECK_FINITE): " + g_hip_detail;
       return s.c_str();
     default: return "unknown status";
   }

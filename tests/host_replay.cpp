@@ -88,7 +88,16 @@ static int rec(const char* phase, int tile, const MatDesc* d, const int64_t* pre
   g_log.push_back(l);
   return 0;
 }
+// The momentum stand-in can leave a chosen value in one descriptor's norm
+// slot, as the momentum pass does for a matrix with a non-finite entry.
+int g_plant_desc = -1;
+double g_plant_value = 0.0;
+double* g_planted_slot = nullptr;
 int launch_momentum_norm(const MatDesc* d, const int64_t* p, int n, int64_t u, float, const float*, int, void*) {
+  if (g_plant_desc >= 0 && g_plant_desc < n) {
+    g_planted_slot = d[g_plant_desc].nrm2;
+    *g_planted_slot = g_plant_value;
+  }
   return rec("momentum", 0, d, p, n, u);
 }
 int launch_normalize(const MatDesc* d, const int64_t* p, int n, int64_t u, float, float, const float*, void*) {
@@ -395,6 +404,90 @@ static void check_call(const char* name, const Case& cs, std::vector<muon_matrix
   }
 }
 
+// MUON_CHECK_FINITE: a step reads back the momentum norms and reports the
+// first non-finite one by the caller's matrix index, on the eager path (first
+// call and the cached repeat) and on a plan step; without the variable the
+// same planted value passes unnoticed.
+static void finite_check(const Case& cs) {
+  const int64_t n = static_cast<int64_t>(cs.shapes.size());
+  std::vector<muon_matrix_t> mats(n);
+  for (int64_t i = 0; i < n; ++i) {
+    muon_matrix_t& m = mats[i];
+    m.rows = cs.shapes[i].first;
+    m.cols = cs.shapes[i].second;
+    m.grad_dtype = MUON_BF16;
+    m.scale = 0.f;
+    const uintptr_t base = 0x100000000000ull + static_cast<uintptr_t>(i) * 0x100000000ull;
+    m.param = reinterpret_cast<float*>(base);
+    m.momentum = reinterpret_cast<float*>(base + 0x40000000ull);
+    m.grad = cs.present.empty() || cs.present[i] ? reinterpret_cast<void*>(base + 0x80000000ull) : nullptr;
+  }
+  const size_t ws_bytes = muon_workspace_bytes(mats.data(), n);
+  char* raw = static_cast<char*>(std::malloc(ws_bytes + 256));
+  char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(raw) + 255) & ~uintptr_t(255));
+  const int nc = static_cast<int>(cs.coeffs.size());
+  auto step = [&]() {
+    return muon_step(mats.data(), n, 0.02f, 0.95f, 0.01f, cs.ns, cs.coeffs.data(), nc, cs.rms, 1e-7f,
+                     ws, ws_bytes, nullptr);
+  };
+  // the caller's index of the planted slot
+  auto planted_index = [&]() -> int64_t {
+    for (int64_t i = 0; i < n; ++i) {
+      muon_workspace_view_t v;
+      if (muon_workspace_view(mats.data(), n, i, cs.ns, &v) == MUON_OK &&
+          reinterpret_cast<double*>(ws + v.nrm2_off) == g_planted_slot)
+        return i;
+    }
+    return -1;
+  };
+  unsetenv("MUON_CHECK_FINITE");
+  g_plant_desc = 0;
+  g_plant_value = std::nan("");
+  CHECK(step() == MUON_OK, "finite: unchecked step with a NaN norm");
+  setenv("MUON_CHECK_FINITE", "1", 1);
+  g_plant_desc = -1;
+  CHECK(step() == MUON_OK, "finite: checked step, all finite");
+  int n_active = 0;
+  for (const auto& l : g_log)
+    if (l.phase == "momentum") n_active = l.n;
+  CHECK(n_active > 2, "finite: %d active descriptors", n_active);
+  const int picks[3] = {0, n_active / 2, n_active - 1};
+  for (int k : picks) {
+    for (int kind = 0; kind < 2; ++kind) {
+      g_plant_desc = k;
+      g_plant_value = kind == 0 ? std::nan("") : HUGE_VAL;
+      for (int rep = 0; rep < 2; ++rep) {            // the first call and the cached repeat
+        g_log.clear();
+        const int rc = step();
+        const int64_t want = planted_index();
+        CHECK(want >= 0 && (cs.present.empty() || cs.present[static_cast<size_t>(want)]),
+              "finite: planted slot %d maps to no active matrix", k);
+        CHECK(rc == MUON_ENONFINITE, "finite: descriptor %d kind %d rep %d gave %d", k, kind, rep, rc);
+        const std::string msg = muon_status_string(rc);
+        const std::string tag = "matrix " + std::to_string(want) + ":";
+        CHECK(msg.find(tag) != std::string::npos && msg.find(kind == 0 ? "NaN" : "infinite") != std::string::npos,
+              "finite: status '%s' does not name %s", msg.c_str(), tag.c_str());
+      }
+    }
+  }
+  // a plan step checks too
+  g_plant_desc = n_active - 1;
+  g_plant_value = std::nan("");
+  muon_plan_t* plan = nullptr;
+  int rc = muon_plan_create(mats.data(), n, cs.ns, cs.coeffs.data(), nc, cs.rms, 1e-7f, nullptr, ws,
+                            ws_bytes, nullptr, &plan);
+  CHECK(rc == MUON_OK, "finite: plan create %d", rc);
+  const float hyper[3] = {0.02f, 0.95f, 0.01f};
+  if (rc == MUON_OK) {
+    rc = muon_plan_step(plan, hyper, nullptr);
+    CHECK(rc == MUON_ENONFINITE, "finite: plan step gave %d", rc);
+    muon_plan_destroy(plan);
+  }
+  unsetenv("MUON_CHECK_FINITE");
+  g_plant_desc = -1;
+  std::free(raw);
+}
+
 int main(int argc, char** argv) {
   const std::string which = argc > 1 ? argv[1] : "all";
   Case mamba;
@@ -465,6 +558,7 @@ int main(int argc, char** argv) {
     const std::string nm = "random " + std::to_string(seed);
     run_case(nm.c_str(), rc);
   }
+  if (which == "all" || which == "finite") finite_check(mixed);
   if (which == "all" || which == "mamba") run_case("mamba", mamba);
   if (which == "all" || which == "transformer") run_case("transformer", transformer);
   if (which == "all" || which == "ragged") run_case("ragged", ragged);

@@ -182,3 +182,42 @@ def test_transpose_equivariance(cls):
     say(f"  {cls} {r}x{c}: O(G^T) vs O(G)^T rel {err:.3e}, bit-identical {same}")
     assert same, f"O(G^T) differs from O(G)^T: rel {err:.3e}"
     assert np.array_equal(run.param(1), run.param(0).T)
+
+
+def test_check_finite_names_the_matrix(monkeypatch):
+    """MUON_CHECK_FINITE: the step reads back the momentum norms and fails
+    with MUON_ENONFINITE naming the first matrix whose norm is NaN or
+    infinite, for an eager step and a plan step; the step itself has run (the
+    other matrices match the oracle); a clean list passes; unset, the same
+    call succeeds."""
+    import torch
+
+    lr, mu, wd = 0.02, 0.95, 0.01
+    shapes = [(64, 96), (256, 768), (1024, 1536), (768, 256)]
+    inputs = [W.adhoc_inputs(r, c, "bf16", seed=130 + i) for i, (r, c) in enumerate(shapes)]
+    bad = 2
+    inputs[bad].grad_bits[5, 7] = _BF16_BITS["nan"]
+    inputs[bad].grad[5, 7] = np.float32(np.nan)
+    monkeypatch.setenv("MUON_CHECK_FINITE", "1")
+    run = Run(inputs)
+    with pytest.raises(muon.LibMuonError) as ei:
+        run.step(lr=lr, mu=mu, wd=wd)
+    torch.cuda.synchronize()
+    assert ei.value.status == muon.MUON_ENONFINITE and f"matrix {bad}:" in str(ei.value), str(ei.value)
+    say(f"  eager: {ei.value}")
+    for i, mi in enumerate(inputs):
+        if i != bad:
+            out = O.muon_step_matrix(mi.param, mi.grad, mi.mom, lr=lr, mu=mu, wd=wd)
+            assert rel(run.o(i), out["o"]) <= TOL_NS
+    # a plan step over the same buffers reports it too
+    plan = muon.Plan(run.p, run.g, run.m, lr=lr, mu=mu, wd=wd, workspace=run.ws)
+    with pytest.raises(muon.LibMuonError) as ei:
+        plan.step()
+    torch.cuda.synchronize()
+    assert ei.value.status == muon.MUON_ENONFINITE and f"matrix {bad}:" in str(ei.value)
+    plan.close()
+    # a clean list passes with the check on, and the NaN list passes with it off
+    clean = [W.adhoc_inputs(r, c, "bf16", seed=140 + i) for i, (r, c) in enumerate(shapes)]
+    Run(clean).step(lr=lr, mu=mu, wd=wd)
+    monkeypatch.delenv("MUON_CHECK_FINITE")
+    Run(inputs).step(lr=lr, mu=mu, wd=wd)

@@ -157,9 +157,16 @@ def test_orthogonalize_argument_errors(lib):
 
 def test_status_strings(lib):
     for st in (muon.MUON_OK, muon.MUON_EINVAL, muon.MUON_EWORKSPACE, muon.MUON_EALIAS, muon.MUON_EHIP,
-               muon.MUON_ECAPTURE, -99):
+               muon.MUON_ECAPTURE, muon.MUON_ENONFINITE, -99):
         assert isinstance(muon.status_string(st), str) and muon.status_string(st)
     assert "captur" in muon.status_string(muon.MUON_ECAPTURE)
+    assert "non-finite" in muon.status_string(muon.MUON_ENONFINITE)
+    # the binding's status values are the header's
+    header = open(os.path.join(ROOT, "include", "muon.h")).read()
+    for name in ("MUON_OK", "MUON_EINVAL", "MUON_EWORKSPACE", "MUON_EHIP", "MUON_EALIAS",
+                 "MUON_ECAPTURE", "MUON_ENONFINITE"):
+        m = re.search(r"#define\s+" + name + r"\s+(-?\d+)", header)
+        assert m and int(m.group(1)) == getattr(muon, name), name
     with pytest.raises(muon.LibMuonError):
         _lib.check(muon.MUON_EINVAL, "x")
 

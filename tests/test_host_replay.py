@@ -9,8 +9,12 @@ absent gradients, 0 to 12 steps, every accepted variant combination, RMS scale
 on or off, through muon_step_ex, a prepared plan or muon_orthogonalize).  The
 harness checks the launch sequence, the prefix arrays against the tile counts,
 and every descriptor's workspace buffers (inside, aligned, disjoint, sized for
-the padded shape) in the table the dispatcher uploaded.  A second build runs
-the same replay under AddressSanitizer."""
+the padded shape) in the table the dispatcher uploaded.  The "finite" case
+plants a NaN or infinite value in one norm slot from the momentum stand-in
+and checks that MUON_CHECK_FINITE reports it by the caller's matrix index (a
+first call, the cached repeat and a plan step), and that nothing is reported
+without the variable.  A second build runs the same replay under
+AddressSanitizer."""
 import os
 import shutil
 import subprocess
@@ -43,7 +47,7 @@ def _run(exe, *args):
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout[-2000:] + r.stderr[-2000:]
 
 
-@pytest.mark.parametrize("case", ["mamba", "transformer", "ragged", "mixed"])
+@pytest.mark.parametrize("case", ["mamba", "transformer", "ragged", "mixed", "finite"])
 def test_dispatcher_replay(replay, case):
     _run(replay, case)
 
@@ -56,6 +60,6 @@ def test_dispatcher_replay_random_lists(replay, seed):
 def test_dispatcher_replay_under_address_sanitizer(tmp_path):
     exe = _build(str(tmp_path / "host_replay_asan"), ("-fsanitize=address", "-fno-omit-frame-pointer"))
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
-    for args in (["mixed"], ["ragged"], *(["random", str(s)] for s in range(8))):
+    for args in (["mixed"], ["ragged"], ["finite"], *(["random", str(s)] for s in range(8))):
         r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=300, env=env)
         assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout[-1000:] + r.stderr[-2000:]
